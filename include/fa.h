@@ -1,0 +1,106 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library for MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention computed tile by tile:
+ * the forward pass keeps each block of scores on chip, folds it into the
+ * output with the online running-maximum softmax, and saves only one
+ * statistic per query row; the backward pass rebuilds every score block from
+ * Q, K and that statistic instead of reading a stored N x N matrix
+ * (dmarx anthology record SOTA-087, "Why recomputation is cheaper here than
+ * storing" and "Condition"; Brenndoerfer, "FlashAttention Algorithm >
+ * Recomputation Strategy", section "What Gets Stored vs Recomputed").
+ *
+ * Mathematics (per batch b, head h; L = valid length of sequence b):
+ *   allowed(i,j) = i < L  and  j < L  and  (!causal or j <= i)
+ *   S_ij   = scale * q_i . k_j  where allowed, -inf elsewhere
+ *   lse_i  = ln sum_j exp(S_ij)           (natural log, scale included)
+ *   P_ij   = exp(S_ij - lse_i),  o_i = sum_j P_ij v_j
+ *   rows i >= L: o_i = 0, lse_i = -inf, and every gradient of row i is 0.
+ * Backward of f = sum(o * dO):  dV = P^T dO;  dP = dO V^T;
+ *   dS_ij = P_ij (dP_ij - D_i) with D_i = dO_i . o_i;
+ *   dQ = scale * dS K;  dK = scale * dS^T Q.
+ *
+ * Layout: q, k, v, o, dO, dq, dk, dv are contiguous [B, H, N, d] arrays,
+ * d fastest, of element type `dtype`, on the device, 16-byte aligned.
+ * lse is a contiguous float32 [B, H, N] device array.  seqlens is NULL (every
+ * sequence has length N) or a device int32 [B] array; each value is clamped
+ * to [0, N] on the device.
+ *
+ * Ownership: the caller allocates and frees every buffer, including the
+ * backward workspace; the library never allocates or frees device memory and
+ * keeps no pointer after a call returns (kernels already queued on `stream`
+ * still read and write the buffers until they finish).  The library holds
+ * no mutable global state, so calls from several threads are safe.
+ *
+ * Ordering: every call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns; the caller synchronises.
+ *
+ * Errors: every entry point returns an fa_status.  Invalid arguments are
+ * reported before any HIP call and have no side effects.  FA_ERR_HIP means a
+ * kernel launch failed; the HIP error state is cleared before returning.
+ * Calls whose B, H or N is 0 do nothing and return FA_OK.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_BF16 = 0, /* bfloat16 inputs/outputs; MFMA bf16 x bf16 -> fp32 */
+  FA_FP32 = 1  /* float32 inputs/outputs; MFMA fp32 -> fp32, P never rounded */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scale or dtype */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_HIP = -4          /* a kernel launch failed */
+} fa_status;
+
+/*
+ * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32).
+ * The score matrix exists only tile by tile in registers; no N x N buffer is
+ * ever formed (SOTA-087, "Why recomputation is cheaper here than storing").
+ * scale must be finite and > 0.  d must be 64 or 128.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* seqlens, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
+ * [B,H,N,d] plus the float32 row vector D [B,H,N] (256-byte aligned parts).
+ * Linear in N.  Returns 0 for empty or invalid shapes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass.  Reads q, k, v, o, dO and the forward's lse; writes dq, dk,
+ * dv (dtype, [B,H,N,d]), fully overwriting them (0 at padded positions).
+ * Recomputes every score block from Q, K and lse instead of reading a stored
+ * probability matrix (Brenndoerfer, "What Gets Stored vs Recomputed").
+ * `workspace` (device, 256-byte aligned, at least fa_bwd_workspace_bytes())
+ * is scratch owned by the caller; its contents on entry are ignored.
+ * dQ is summed over key blocks with float32 atomics, so dq may differ in the
+ * last bits from run to run; o, lse, dk and dv are deterministic.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+           int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,93 @@
+// C ABI of the attention library: argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Declarations and the full contract are in
+// include/fa.h.  Nothing here allocates device memory.
+#include "fa.h"
+
+#include <math.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kMaxN = 1 << 24;  // per-head row offsets stay within 32-bit arithmetic
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common shape/scalar checks.  Returns FA_OK, an error, or 1 for "empty: nothing to do".
+int check_common(int B, int H, int N, int d, float scale, int dtype) {
+  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || N < 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
+  if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (B == 0 || H == 0 || N == 0) return 1;
+  return FA_OK;
+}
+
+bool tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, const int32_t* seqlens, int dtype, void* stream) {
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, seqlens, B, H, N, scale};
+  hipError_t e = fa::launch_fwd(a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  int st = check_common(B, H, N, d, 1.0f, dtype);
+  if (st != FA_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens,
+           void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dO)) return FA_ERR_INVALID_ARG;
+  if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv)) return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
+  if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  float* dq_acc = static_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float), 256));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, seqlens, B, H, N, scale};
+  hipError_t e = fa::launch_bwd(a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

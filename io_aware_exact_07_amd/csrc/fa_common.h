@@ -1,0 +1,173 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used everywhere (v_mfma_f32_32x32x16_bf16; the
+// fp32 path issues eight v_mfma_f32_32x32x2_f32 per 16-wide chunk with the
+// same register arrangement):
+//   A fragment  lane l: row m = l % 32, contraction k = 8*(l/32) + e, e = 0..7
+//   B fragment  lane l: col n = l % 32, contraction k = 8*(l/32) + e
+//   C/D tile    lane l: col n = l % 32, register i: row acc_row(i, l/32)
+// A "row fragment" is 8 contraction-contiguous elements of one row, read with
+// one 16-byte LDS load.  A "column fragment" holds 8 contraction indices that
+// are 8 different rows of a row-major LDS tile; for bf16 it is gathered with
+// two ds_read_b64_tr_b16, whose lane mapping is: within each group of 16
+// lanes, lane 4r+s supplies the address of 4 contiguous elements of row r
+// (columns 4s..4s+3 of a 16-column strip) and lane j receives column j of
+// rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16> { using type = bf16x8; };
+template <> struct FragOf<float> { using type = f32x8; };
+template <typename T> using Frag = typename FragOf<T>::type;
+
+// Row of the 32x32 accumulator held in register i by lanes of half h.
+__device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ void mma16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 8 contiguous elements at p (16-byte aligned for bf16, 32-byte span for fp32).
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
+  return r;
+}
+template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
+  Frag<T> z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (T)0.f;
+  return z;
+}
+
+// Column fragment from a row-major LDS tile `base` with row stride `stride`
+// elements.  The lane receives column col0 + (lane % 32) of 8 rows.
+// PERM = false: register e holds row k0 + 8*h + e               (h = lane/32)
+// PERM = true:  register e holds row k0 + 8*(e/4) + 4*h + e%4
+// The PERM order is the key order in which a 32x32 accumulator's registers
+// 8c..8c+7 enumerate rows 16c..16c+15, so an accumulator can feed a matrix
+// core directly as the contraction operand against this fragment.
+template <bool PERM>
+__device__ __forceinline__ bf16x8 ld_col_frag(const bf16* base, int stride, int k0, int col0, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, s = lane & 3, h = lane >> 5;
+  const int col = col0 + 16 * (g & 1) + 4 * s;
+  bf16x8 out;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = PERM ? (k0 + 8 * t + 4 * h + r) : (k0 + 8 * h + 4 * t + r);
+    const bf16* p = base + row * stride + col;
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    bf16x4 vb = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * t + e] = vb[e];
+  }
+  return out;
+}
+template <bool PERM>
+__device__ __forceinline__ f32x8 ld_col_frag(const float* base, int stride, int k0, int col0, int lane) {
+  const int h = lane >> 5, col = col0 + (lane & 31);
+  f32x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = PERM ? (k0 + 8 * (e >> 2) + 4 * h + (e & 3)) : (k0 + 8 * h + e);
+    out[e] = base[row * stride + col];
+  }
+  return out;
+}
+
+// Store 4 consecutive values (converted to T) at p.
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Exchange with the lane 32 apart: returns {x, partner} in some order, so
+// max/sum of the pair is the same on both halves.
+__device__ __forceinline__ float pair_max(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Copies rows [r0, r0+R) of a row-major [nrows][D] global array into an LDS
+// tile with row stride STR, through registers so the global load can be
+// issued early and the LDS store later.  Rows >= nrows are zero-filled.
+template <typename T, int R, int D, int NT>
+struct TileCopy {
+  static constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;          // chunks per row
+  static constexpr int TOTAL = R * CPR;
+  static_assert(TOTAL % NT == 0, "tile must split evenly over the threads");
+  static constexpr int PER = TOTAL / NT;
+  uint4 buf[PER];
+
+  __device__ __forceinline__ void load(const T* g, int r0, int nrows, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * NT;
+      const int row = c / CPR, col = (c % CPR) * EPC;
+      if (r0 + row < nrows)
+        buf[u] = *reinterpret_cast<const uint4*>(g + (size_t)(r0 + row) * D + col);
+      else
+        buf[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  template <int STR>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + u * NT;
+      const int row = c / CPR, col = (c % CPR) * EPC;
+      *reinterpret_cast<uint4*>(lds + row * STR + col) = buf[u];
+    }
+  }
+};
+
+__device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
+  if (!seqlens) return N;
+  int L = seqlens[b];
+  return L < 0 ? 0 : (L > N ? N : L);
+}
+
+}  // namespace fa

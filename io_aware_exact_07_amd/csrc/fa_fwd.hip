@@ -1,0 +1,188 @@
+// Forward pass of exact tiled attention on gfx950.
+//
+// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
+// owns 32 rows.  Key/value blocks of 64 rows are streamed through LDS
+// (double buffered, one barrier per block) and every block of scores lives
+// only in registers: it is produced by the matrix cores, folded into the
+// running max / normaliser / output accumulator, and dropped (dmarx anthology
+// record SOTA-087, "Why recomputation is cheaper here than storing": the score
+// block is consumed on chip and never written out; "Condition": the softmax is
+// computed blockwise with the online running-maximum formulation).
+//
+// Orientation: each wave computes S^T = K Q^T, so a lane owns one query and
+// holds that query's scores for 16 keys of each 32-key tile; the row max and
+// row sum are in-lane reductions plus one exchange with the lane 32 apart.
+// The output is accumulated transposed (O^T += V^T P^T) so that the running
+// rescale factor of a query is a per-lane scalar, and the probability tile is
+// fed to the matrix core straight from registers (the V^T fragment is read
+// with the matching key order).
+//
+// Saved per row: lse = m*scale + ln(l), one float32, which is everything the
+// backward pass needs besides Q, K, V, O (Brenndoerfer, "FlashAttention
+// Algorithm > Recomputation Strategy", "What Gets Stored vs Recomputed": the
+// running max m and normaliser L; stored here as their combination).
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kFwdBQ = 128;
+constexpr int kFwdBK = 64;
+constexpr int kFwdThreads = 256;
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
+  constexpr int BQ = kFwdBQ, BK = kFwdBK, NT = kFwdThreads;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int STR = D + PAD;
+  constexpr int NC = D / 16;   // contraction chunks over the head dimension
+  constexpr int NDT = D / 32;  // 32-wide output tiles over the head dimension
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * STR];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * STR];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + BQ - 1) / BQ;
+  // Causal: heaviest query blocks (most keys) are dispatched first.
+  const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.H;
+  const int L = clamp_len(a.seqlens, b, a.N);
+  const size_t hoff = (size_t)bh * a.N * D;
+  const T* Q = reinterpret_cast<const T*>(a.q) + hoff;
+  const T* K = reinterpret_cast<const T*>(a.k) + hoff;
+  const T* V = reinterpret_cast<const T*>(a.v) + hoff;
+  T* O = reinterpret_cast<T*>(a.o) + hoff;
+  float* LSE = a.lse + (size_t)bh * a.N;
+
+  const int q0w = qb * BQ + w * 32;  // first query row of this wave
+  const int qrow = q0w + n;          // this lane's query row
+  int kend = L;                      // keys needed by the workgroup
+  if (CAUSAL) kend = min(kend, min(a.N, (qb + 1) * BQ));
+  int kend_w = L;                    // keys needed by this wave
+  if (CAUSAL) kend_w = min(kend_w, q0w + 32);
+  const bool wave_live = q0w < L;
+
+  Frag<T> qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qf[c] = (qrow < a.N) ? ld8(Q + (size_t)qrow * D + 16 * c + 8 * h) : zero_frag<T>();
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = zero16();
+  float m = -1e30f;   // running max of raw scores (finite sentinel: no inf-inf)
+  float lsum = 0.f;   // this lane's half of the running normaliser
+  const float c2 = a.scale * kLog2e;
+
+  const int nkb = (kend + BK - 1) / BK;
+  TileCopy<T, BK, D, NT> ck, cv;
+  if (nkb > 0) {
+    ck.load(K, 0, a.N, tid);
+    cv.load(V, 0, a.N, tid);
+  }
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    ck.template store<STR>(sK[buf], tid);
+    cv.template store<STR>(sV[buf], tid);
+    __syncthreads();
+    if (kb + 1 < nkb) {
+      ck.load(K, (kb + 1) * BK, a.N, tid);
+      cv.load(V, (kb + 1) * BK, a.N, tid);
+    }
+    const int k0 = kb * BK;
+    if (wave_live && k0 < kend_w) {
+      const T* kt = sK[buf];
+      const T* vt = sV[buf];
+      f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) mma16(s[t], ld8(kt + (t * 32 + n) * STR + 16 * c + 8 * h), qf[c]);
+
+      const bool edge = (k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w);
+      if (edge) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * t + acc_row(i, h);
+            if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+      mx = pair_max(mx);
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_fast((m - mnew) * c2);
+      m = mnew;
+      const float mc = mnew * c2;
+      float rs = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(fmaf(s[t][i], c2, -mc));
+          s[t][i] = p;
+          rs += p;
+        }
+      lsum = lsum * alpha + rs;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+
+      // P^T as contraction operand: chunk c covers keys 16c..16c+15 of the
+      // block, registers 8*(c%2)..+7 of tile c/2 (the PERM key order).
+      Frag<T> pf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[c][e] = (T)s[c >> 1][8 * (c & 1) + e];
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mma16(acc[t], ld_col_frag<true>(vt, STR, 16 * c, 32 * t, lane), pf[c]);
+    }
+  }
+
+  const float ltot = pair_sum(lsum);
+  if (qrow < a.N) {
+    const bool valid = qrow < L;
+    const float inv = valid ? 1.f / ltot : 0.f;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        st4(O + (size_t)qrow * D + 32 * t + 8 * gi + 4 * h, acc[t][4 * gi] * inv, acc[t][4 * gi + 1] * inv,
+            acc[t][4 * gi + 2] * inv, acc[t][4 * gi + 3] * inv);
+    if (h == 0) LSE[qrow] = valid ? (m * a.scale + log2_fast(ltot) * kLn2) : -INFINITY;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.N + kFwdBQ - 1) / kFwdBQ;
+  const long long grid = (long long)nqb * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kFwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool causal, hipStream_t stream) {
+  if (dtype == 0) {
+    if (d == 64) return causal ? launch_one<bf16, 64, true>(a, stream) : launch_one<bf16, 64, false>(a, stream);
+    return causal ? launch_one<bf16, 128, true>(a, stream) : launch_one<bf16, 128, false>(a, stream);
+  }
+  if (d == 64) return causal ? launch_one<float, 64, true>(a, stream) : launch_one<float, 64, false>(a, stream);
+  return causal ? launch_one<float, 128, true>(a, stream) : launch_one<float, 128, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,111 @@
+"""GPU properties beyond parity: determinism, exact special cases, guard bands,
+empty inputs and linear memory."""
+import math
+
+import pytest
+import torch
+
+import io_aware_exact_07_amd as fa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = "cuda:0"
+
+
+def test_forward_is_bitwise_deterministic():
+    inp = W.random_inputs(2, 3, 700, 64, "bf16", seed=5, gain=2.0)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    do = inp["do"].to(DEV)
+    g1 = fa.backward(q, k, v, o1, do, l1, causal=True)
+    g2 = fa.backward(q, k, v, o1, do, l1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])  # dK, dV have no atomics
+    assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-2 * g1[0].float().abs().max().item()
+
+
+def test_zero_queries_give_prefix_means():
+    B, H, N, d = 1, 2, 300, 64
+    inp = W.random_inputs(B, H, N, d, "fp32", seed=9)
+    q = torch.zeros(B, H, N, d, device=DEV)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    o, lse = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    ref = torch.cumsum(inp["v"].double(), dim=2) / torch.arange(1, N + 1, dtype=torch.float64)[None, None, :, None]
+    assert (o.cpu().double() - ref).abs().max().item() < 1e-5
+    assert (lse.cpu().double() - torch.log(torch.arange(1, N + 1, dtype=torch.float64))).abs().max().item() < 1e-5
+
+
+def test_outputs_leave_guard_bands_untouched():
+    B, H, N, d = 2, 2, 190, 128
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=3, seqlens=[190, 55])
+    n = B * H * N * d
+    guard = 4096
+    bufs = {}
+    for name in ("o", "dq", "dk", "dv"):
+        t = torch.full((n + 2 * guard,), 7.0, device=DEV, dtype=torch.bfloat16)
+        bufs[name] = t
+    lse_buf = torch.full((B * H * N + 2 * guard,), 7.0, device=DEV)
+    view = lambda t: t[guard:guard + n].view(B, H, N, d)
+    q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+    sl = inp["seqlens"].to(DEV)
+    lse = lse_buf[guard:guard + B * H * N].view(B, H, N)
+    o, _ = fa.forward(q, k, v, causal=False, seqlens=sl, out=view(bufs["o"]), lse=lse)
+    fa.backward(q, k, v, o, do, lse, causal=False, seqlens=sl,
+                grads=(view(bufs["dq"]), view(bufs["dk"]), view(bufs["dv"])))
+    torch.cuda.synchronize()
+    for name, t in list(bufs.items()) + [("lse", lse_buf)]:
+        assert torch.all(t[:guard] == 7.0) and torch.all(t[-guard:] == 7.0), f"{name} guard band written"
+    assert torch.all(view(bufs["o"])[1, :, 55:] == 0)
+
+
+def test_empty_inputs_are_noops():
+    x = torch.empty(0, 2, 128, 64, device=DEV, dtype=torch.bfloat16)
+    o, lse = fa.forward(x, x, x)
+    assert o.shape == x.shape
+    y = torch.empty(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    o, lse = fa.forward(y, y, y)
+    dq, dk, dv = fa.backward(y, y, y, o, y, lse)
+    torch.cuda.synchronize()
+
+
+def test_seqlens_clamped_on_device():
+    inp = W.random_inputs(2, 1, 96, 64, "bf16", seed=12)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o_a, l_a = fa.forward(q, k, v, seqlens=torch.tensor([96, 0], dtype=torch.int32, device=DEV))
+    o_b, l_b = fa.forward(q, k, v, seqlens=torch.tensor([1000, -5], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    assert torch.all(o_a[1] == 0) and torch.all(torch.isneginf(l_a[1]))
+
+
+def test_workspace_and_memory_are_linear_in_N():
+    sizes = [1024, 2048, 4096, 8192]
+    ws = [fa.fa_bwd_workspace_bytes(1, 12, n, 64, fa.FA_BF16) for n in sizes]
+    assert all(b == 2 * a for a, b in zip(ws, ws[1:]))
+    peaks = []
+    for n in sizes:
+        inp = W.random_inputs(1, 12, n, 64, "bf16", seed=1)
+        q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o, lse = fa.forward(q, k, v, causal=True)
+        fa.backward(q, k, v, o, do, lse, causal=True)
+        torch.cuda.synchronize()
+        peaks.append(torch.cuda.max_memory_allocated() - base)
+        del q, k, v, do, o, lse
+    # every byte the path allocates (outputs + workspace) is linear in N: an
+    # N x N fp32 buffer at N = 8192 would be 3.2 GB for 12 heads
+    per_n = [p / n for p, n in zip(peaks, sizes)]
+    assert max(per_n) <= 1.05 * min(per_n), peaks
+    n = sizes[-1]
+    expected = 4 * (12 * n * 64 * 2) + 12 * n * 4 + ws[-1]   # o, dq, dk, dv + lse + workspace
+    assert peaks[-1] <= 1.05 * expected, (peaks[-1], expected)

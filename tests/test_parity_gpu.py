@@ -1,0 +1,147 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases are compared element by element over every output; the five
+full-size workloads are compared on sampled outputs the oracle can compute
+(whole heads, query rows, key rows) plus properties that hold at any size.
+"""
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity_util import TOL, f64, gpu_run, lse_err, rel_err, valid_rows
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def compare_heads(inp, got, causal, scale, heads, dtype):
+    sl = inp.get("seqlens")
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal,
+                                    None if sl is None else sl.numpy(), heads=heads)
+    tol = TOL[dtype]
+    for b, h in heads:
+        L = valid_rows(sl, b, inp["q"].shape[2])
+        for name in ("o", "dq", "dk", "dv"):
+            g = f64(got[name][b, h])
+            r = ref[name][b, h]
+            e = rel_err(g[:L], r[:L]) if L > 0 else 0.0
+            assert e <= tol[name], f"{name} head {(b, h)} rel err {e:.3e} > {tol[name]}"
+            assert np.all(g[L:] == 0), f"{name} padded rows not zero (head {(b, h)})"
+        e = lse_err(f64(got["lse"][b, h]), ref["lse"][b, h])
+        assert e <= tol["lse"], f"lse head {(b, h)} abs err {e:.3e}"
+
+
+SMALL = [
+    # (B, H, N, d, dtype, causal, seqlens)
+    (1, 1, 1, 64, "bf16", False, None),
+    (1, 2, 17, 64, "bf16", True, None),
+    (2, 1, 100, 128, "bf16", False, None),
+    (1, 2, 129, 64, "bf16", True, None),
+    (2, 2, 300, 64, "bf16", True, None),
+    (2, 2, 300, 128, "bf16", False, None),
+    (3, 2, 257, 64, "bf16", False, [257, 1, 130]),
+    (3, 1, 200, 128, "bf16", True, [0, 77, 200]),
+    (2, 1, 190, 64, "fp32", True, None),
+    (2, 1, 160, 128, "fp32", False, [99, 160]),
+    (1, 1, 333, 128, "fp32", True, None),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,seqlens", SMALL)
+def test_small_full_parity(B, H, N, d, dtype, causal, seqlens):
+    say(f"small parity B={B} H={H} N={N} d={d} {dtype} causal={causal} seqlens={seqlens}")
+    inp = W.random_inputs(B, H, N, d, dtype, seed=N + d, gain=1.5, seqlens=seqlens)
+    scale = 1.0 / math.sqrt(d)
+    got = gpu_run(inp, causal, scale)
+    compare_heads(inp, got, causal, scale, [(b, h) for b in range(B) for h in range(H)], dtype)
+
+
+def test_single_head_fp32_workload():
+    w = W.SINGLE_HEAD_FP32
+    say(f"workload {w.name}")
+    inp = W.make_inputs(w)
+    got = gpu_run(inp, w.causal, w.softmax_scale)
+    compare_heads(inp, got, w.causal, w.softmax_scale, [(0, 0)], w.dtype)
+
+
+@pytest.mark.parametrize("w,heads", [
+    (W.GPT2_SMALL, [(0, 0), (3, 7), (7, 11)]),
+    (W.BERT_LARGE_PADDED, [(0, 0), (5, 9), (11, 3), (15, 15)]),
+])
+def test_full_size_whole_heads(w, heads):
+    say(f"workload {w.name}: heads {heads}")
+    inp = W.make_inputs(w)
+    t0 = time.time()
+    got = gpu_run(inp, w.causal, w.softmax_scale)
+    say(f"  gpu done {time.time() - t0:.1f}s")
+    compare_heads(inp, got, w.causal, w.softmax_scale, heads, w.dtype)
+    say(f"  oracle compare done {time.time() - t0:.1f}s")
+    check_invariants(inp, got, w)
+
+
+def check_invariants(inp, got, w):
+    """Properties that hold over the full tensors at any size."""
+    sl = inp.get("seqlens")
+    B, H, N, d = inp["q"].shape
+    dk = got["dk"].to(torch.float64)
+    dv = got["dv"].to(torch.float64)
+    do = inp["do"].to(torch.float64)
+    for b in range(B):
+        L = valid_rows(sl, b, N)
+        # sum over keys of dK is 0; sum over keys of dV equals sum over valid queries of dO
+        s_dk = dk[b, :, :L].sum(dim=1).abs().max().item()
+        s_dv = (dv[b, :, :L].sum(dim=1) - do[b, :, :L].sum(dim=1)).abs().max().item()
+        scale_dk = dk[b].abs().max().item() * math.sqrt(max(L, 1)) + 1e-30
+        scale_dv = do[b].abs().max().item() * math.sqrt(max(L, 1)) + 1e-30
+        assert s_dk <= 0.05 * scale_dk, f"sum dK = {s_dk} (batch {b})"
+        assert s_dv <= 0.05 * scale_dv, f"sum dV - sum dO = {s_dv} (batch {b})"
+        assert torch.all(got["o"][b, :, L:] == 0) and torch.all(got["dq"][b, :, L:] == 0)
+        assert torch.all(torch.isneginf(got["lse"][b, :, L:]))
+    if w.causal:
+        # row 0 attends only key 0: its output is exactly v_0
+        assert torch.equal(got["o"][:, :, 0], inp["v"][:, :, 0])
+
+
+@pytest.mark.parametrize("w,nheads_rows,nkeys", [(W.GPT2_LONG, 12, 256), (W.VERY_LONG, 16, 256)])
+def test_long_context_sampled(w, nheads_rows, nkeys):
+    """256 random query rows in every head (O, LSE, dQ) and 256 random key rows
+    of one head (dK, dV, streaming all queries through the oracle)."""
+    say(f"workload {w.name}")
+    inp = W.make_inputs(w)
+    t0 = time.time()
+    got = gpu_run(inp, w.causal, w.softmax_scale)
+    say(f"  gpu done {time.time() - t0:.1f}s")
+    tol = TOL[w.dtype]
+    rng = np.random.default_rng(w.seed)
+    rows = np.sort(rng.choice(w.N, 256, replace=False))
+    q64, k64, v64, do64 = (f64(inp[n][0]) for n in ("q", "k", "v", "do"))
+    errs = dict(o=0.0, dq=0.0, lse=0.0)
+    for h in range(nheads_rows):
+        O, lse, dq = oracle.rows_forward_backward(q64[h], k64[h], v64[h], do64[h], w.softmax_scale, rows, w.causal)
+        errs["o"] = max(errs["o"], rel_err(f64(got["o"][0, h])[rows], O))
+        errs["dq"] = max(errs["dq"], rel_err(f64(got["dq"][0, h])[rows], dq))
+        errs["lse"] = max(errs["lse"], lse_err(f64(got["lse"][0, h])[rows], lse))
+    say(f"  rows checked {time.time() - t0:.1f}s errs {errs}")
+    assert errs["o"] <= tol["o"] and errs["dq"] <= tol["dq"] and errs["lse"] <= tol["lse"], errs
+    cols = np.sort(rng.choice(w.N, nkeys, replace=False))
+    h = w.H // 2
+    dk, dv = oracle.key_columns_backward(q64[h], k64[h], v64[h], do64[h], w.softmax_scale, cols, w.causal)
+    e_dk = rel_err(f64(got["dk"][0, h])[cols], dk)
+    e_dv = rel_err(f64(got["dv"][0, h])[cols], dv)
+    say(f"  key rows checked {time.time() - t0:.1f}s dk {e_dk:.3e} dv {e_dv:.3e}")
+    assert e_dk <= tol["dk"] and e_dv <= tol["dv"]
+    check_invariants(inp, got, w)

@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + recomputing backward) on one MI355X.
+
+One step = one forward and one backward pass (fa_fwd, then fa_bwd's three
+stages) over the long-context GPT-2 head workload: B=1, H=12, N=8192, d=64,
+bf16, causal, Q and K scaled by 2 (inputs resident in HBM before timing).
+FLOPs are counted as 4*B*H*N^2*d forward and 2.5x that backward, halved for
+the causal mask.
+
+Prints one JSON line.  Besides the whole-step rate it carries:
+  roofline      the kernel with the longest average launch (of the forward,
+                the dK/dV stage and the dQ stage) against the bf16 dense
+                matrix-core peak: its algorithmic FLOPs (2*N^2*d per matrix
+                product per head, halved when causal, times the products the
+                kernel performs: 2 forward, 4 dK/dV, 3 dQ) over its average
+                duration, timed with HIP events on the stream the kernels run
+                on; `traffic` is the HBM bytes per launch from rocprofv3
+                FETCH_SIZE + WRITE_SIZE counters recorded under profiles/ when
+                they were taken on the current kernel source, else null
+  cpu_baseline  the fp64 CPU oracle timed on this host on whole heads of the
+                same workload (about 10 s of work), in the same unit
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-probe   (plain 256 MiB copy, for counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s at 1 MI355X (bf16, d=64, N=1k–32k); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+KERNELS = {
+    # name: (source file, matrix products per score element)
+    "fwd_kernel": ("io_aware_exact_07_amd/csrc/fa_fwd.hip", 2),
+    "bwd_dkdv_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 4),
+    "bwd_dq_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 3),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNELS[kernel][0], "io_aware_exact_07_amd/csrc/fa_common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_file(kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_gpt2_long_traffic.txt")
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` on this workload, if the recorded
+    counters were taken on the current kernel source."""
+    path = traffic_file(kernel)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    import torch
+    n = 256 * 1024 * 1024
+    x = torch.ones(n // 4, device="cuda:0", dtype=torch.float32)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    """The oracle as it stands, on whole heads of the workload (as many as fit
+    in about min_seconds, at least one), on this host's cores."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inp = W.make_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for bh in heads:
+        oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.softmax_scale, w.causal, heads=[bh])
+        done += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    f_fwd, f_bwd = w.flops()
+    flops = (f_fwd + f_bwd) * done / len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of the same workload, full forward + backward in float64 "
+                      f"numpy; {dt:.2f} s for {flops / 1e9:.1f} counted GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"heads shard across GPUs with no exchange, so per-GPU throughput is the N=1 figure.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+    import io_aware_exact_07_amd as fa
+    import workloads as W
+
+    w = W.GPT2_LONG
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsb = fa.fa_bwd_workspace_bytes(B, H, N, d, fa.FA_BF16)
+    ws = torch.empty(wsb, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    scale = w.softmax_scale
+    P = [t.data_ptr() for t in (q, k, v, o, lse, dq, dk, dv, do, ws)]
+
+    def step(ev=None):
+        st = fa.fa_fwd(P[0], P[1], P[2], P[3], P[4], B, H, N, d, scale, 1, None, fa.FA_BF16, sp)
+        if ev is not None:
+            ev[0].record(stream)
+        st |= fa.fa_bwd_prepare(P[3], P[8], B, H, N, d, None, P[9], wsb, fa.FA_BF16, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= fa.fa_bwd_dkdv(P[0], P[1], P[2], P[8], P[4], P[6], P[7], B, H, N, d, scale, 1, None, P[9], wsb,
+                             fa.FA_BF16, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        st |= fa.fa_bwd_dq(P[0], P[1], P[2], P[8], P[4], P[5], B, H, N, d, scale, 1, None, P[9], wsb, fa.FA_BF16,
+                           sp)
+        if ev is not None:
+            ev[3].record(stream)
+        if st != 0:
+            raise RuntimeError(f"attention call failed: {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    starts = [mk() for _ in range(K)]
+    marks = [[mk(), mk(), mk(), mk()] for _ in range(K)]
+    t_begin, t_end = mk(), mk()
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(K):
+        starts[i].record(stream)
+        step(marks[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    ms = total_ms / K
+    avg = lambda f: sum(f(i) for i in range(K)) / K
+    fwd_ms = avg(lambda i: starts[i].elapsed_time(marks[i][0]))
+    prep_ms = avg(lambda i: marks[i][0].elapsed_time(marks[i][1]))
+    dkdv_ms = avg(lambda i: marks[i][1].elapsed_time(marks[i][2]))
+    dq_ms = avg(lambda i: marks[i][2].elapsed_time(marks[i][3]))
+    bwd_ms = prep_ms + dkdv_ms + dq_ms
+
+    f_fwd, f_bwd = w.flops()
+    value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    per_product = f_fwd / 2.0
+    launches = {"fwd_kernel": fwd_ms, "bwd_dkdv_kernel": dkdv_ms, "bwd_dq_kernel": dq_ms}
+    dom = max(launches, key=launches.get)
+    achieved = KERNELS[dom][1] * per_product / (launches[dom] * 1e-3) / 1e12
+    e = 2
+    compulsory = e * 4 * B * H * N * d + 4 * B * H * N                 # forward: q, k, v, o + lse
+    compulsory += e * 2 * B * H * N * d + 4 * B * H * N                # prepare: o, dO -> D
+    compulsory += 2 * (e * 4 * B * H * N * d + 8 * B * H * N)          # dkdv, dq: q, k, v, dO, lse, D in
+    compulsory += e * 3 * B * H * N * d                                # dk, dv, dq out
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": True,
+                   "fwd_gflop": f_fwd / 1e9, "bwd_gflop": f_bwd / 1e9},
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv": round(dkdv_ms, 5), "dq": round(dq_ms, 5)},
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "compulsory_hbm_gbs": round(compulsory / (ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": recorded_traffic(dom),
+            "avg_launch_ms": round(launches[dom], 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

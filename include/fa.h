@@ -74,9 +74,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* seqlens, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
- * [B,H,N,d] plus the float32 row vector D [B,H,N] (256-byte aligned parts).
- * Linear in N.  Returns 0 for empty or invalid shapes.
+ * Bytes of device workspace fa_bwd needs: the float32 row vector
+ * D [B,H,N] (D_i = dO_i . o_i), rounded up to 256 bytes.  Linear in N.
+ * Returns 0 for empty or invalid shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
@@ -85,16 +85,42 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  * dv (dtype, [B,H,N,d]), fully overwriting them (0 at padded positions).
  * Recomputes every score block from Q, K and lse instead of reading a stored
  * probability matrix (Brenndoerfer, "What Gets Stored vs Recomputed").
- * `workspace` (device, 256-byte aligned, at least fa_bwd_workspace_bytes())
+ * `workspace` (device, 16-byte aligned, at least fa_bwd_workspace_bytes())
  * is scratch owned by the caller; its contents on entry are ignored.
- * dQ is summed over key blocks with float32 atomics, so dq may differ in the
- * last bits from run to run; o, lse, dk and dv are deterministic.
+ * Deterministic: every output is bitwise reproducible run to run.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            const int32_t* seqlens, void* workspace, size_t workspace_bytes,
            int dtype, void* stream);
+
+/*
+ * The three launches fa_bwd makes, exposed for callers that time them
+ * separately or run the two gradient stages concurrently.  Calling prepare,
+ * then dkdv and dq (in either order, or on two streams ordered after
+ * prepare) with one workspace is exactly fa_bwd.
+ *   prepare: D_i = dO_i . o_i into the workspace (reads o, dO).  A row of
+ *            the softmax-Jacobian product reduces to dS_ij = P_ij (dP_ij - D_i)
+ *            because sum_j P_ij dP_ij = dO_i . o_i.
+ *   dkdv:    recomputes the score blocks key block by key block and writes
+ *            dk and dv (reads q, k, v, dO, lse and the prepared workspace).
+ *   dq:      recomputes the score blocks query block by query block and
+ *            writes dq (same inputs).
+ * Validation and errors are as for fa_bwd; each stage checks only the
+ * pointers it uses (the others may be NULL).
+ */
+int fa_bwd_prepare(const void* o, const void* dO, int B, int H, int N, int d,
+                   const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                   int dtype, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                const float* lse, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, const int32_t* seqlens, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+              const float* lse, void* dq, int B, int H, int N, int d,
+              float scale, int causal, const int32_t* seqlens, void* workspace,
+              size_t workspace_bytes, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);

@@ -6,7 +6,8 @@ PyTorch supplies device memory and the stream.  If the library has not been
 built the import of the native part fails loudly; there is no fallback.
 
 Raw entry points (same names and argument order as the C ABI, pointers as
-ints): fa_fwd, fa_bwd, fa_bwd_workspace_bytes, fa_status_string.
+ints): fa_fwd, fa_bwd, fa_bwd_prepare, fa_bwd_dkdv, fa_bwd_dq,
+fa_bwd_workspace_bytes, fa_status_string.
 Tensor helpers: forward(q, k, v, ...) -> (o, lse) and
 backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv).
 """
@@ -51,6 +52,12 @@ def lib():
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
         L.fa_bwd.restype = ci
+        L.fa_bwd_prepare.argtypes = [vp, vp, ci, ci, ci, ci, vp, vp, sz, ci, vp]
+        L.fa_bwd_prepare.restype = ci
+        L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
+        L.fa_bwd_dkdv.restype = ci
+        L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
+        L.fa_bwd_dq.restype = ci
         L.fa_status_string.argtypes = [ci]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -67,6 +74,22 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, 
            dtype, stream) -> int:
     return lib().fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, int(bool(causal)), seqlens,
                         workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_prepare(o, dO, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream) -> int:
+    return lib().fa_bwd_prepare(o, dO, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, scale, causal, seqlens, workspace, workspace_bytes,
+                dtype, stream) -> int:
+    return lib().fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, scale, int(bool(causal)), seqlens,
+                             workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, scale, causal, seqlens, workspace, workspace_bytes, dtype,
+              stream) -> int:
+    return lib().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, scale, int(bool(causal)), seqlens, workspace,
+                           workspace_bytes, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:

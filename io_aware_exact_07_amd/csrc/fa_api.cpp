@@ -51,32 +51,87 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   int st = check_common(B, H, N, d, 1.0f, dtype);
   if (st != FA_OK) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+  return round_up((size_t)B * H * N * sizeof(float), 256);
 }
+
+namespace {
+
+enum Stage { kAll = 0, kPrepare = 1, kDkDv = 2, kDq = 3 };
+
+// Shared validation of the backward entry points; fills `a` on success.
+int bwd_setup(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens,
+              void* workspace, size_t workspace_bytes, int dtype, int stage, fa::BwdArgs* a) {
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  const bool compute = stage == kAll || stage == kDkDv || stage == kDq;
+  if (compute && (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v))) return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kPrepare) && !tensor_ok(o)) return FA_ERR_INVALID_ARG;
+  if (!tensor_ok(dO)) return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kDkDv) && (!tensor_ok(dk) || !tensor_ok(dv))) return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kDq) && !tensor_ok(dq)) return FA_ERR_INVALID_ARG;
+  if (compute && (lse == nullptr || !aligned(lse, 4))) return FA_ERR_INVALID_ARG;
+  if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
+  if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  *a = fa::BwdArgs{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), seqlens, B, H, N, scale};
+  return FA_OK;
+}
+
+int run_stages(int first, int last, const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
+  for (int s = first; s <= last; ++s) {
+    hipError_t e = fa::launch_bwd_stage(s, a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return FA_ERR_HIP;
+    }
+  }
+  return FA_OK;
+}
+
+}  // namespace
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens,
            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  int st = check_common(B, H, N, d, scale, dtype);
+  fa::BwdArgs a;
+  int st = bwd_setup(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, workspace, workspace_bytes, dtype,
+                     kAll, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dO)) return FA_ERR_INVALID_ARG;
-  if (!tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv)) return FA_ERR_INVALID_ARG;
-  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
-  if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * H * N;
-  float* dq_acc = static_cast<float*>(workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float), 256));
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, seqlens, B, H, N, scale};
-  hipError_t e = fa::launch_bwd(a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
+  return run_stages(kPrepare, kDq, a, d, dtype, causal, stream);
+}
+
+int fa_bwd_prepare(const void* o, const void* dO, int B, int H, int N, int d, const int32_t* seqlens,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  fa::BwdArgs a;
+  int st = bwd_setup(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr, B, H, N, d, 1.0f, seqlens,
+                     workspace, workspace_bytes, dtype, kPrepare, &a);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  return run_stages(kPrepare, kPrepare, a, d, dtype, 0, stream);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  fa::BwdArgs a;
+  int st = bwd_setup(q, k, v, nullptr, dO, lse, nullptr, dk, dv, B, H, N, d, scale, seqlens, workspace,
+                     workspace_bytes, dtype, kDkDv, &a);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  return run_stages(kDkDv, kDkDv, a, d, dtype, causal, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B, int H,
+              int N, int d, float scale, int causal, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+              int dtype, void* stream) {
+  fa::BwdArgs a;
+  int st = bwd_setup(q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, B, H, N, d, scale, seqlens, workspace,
+                     workspace_bytes, dtype, kDq, &a);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  return run_stages(kDq, kDq, a, d, dtype, causal, stream);
 }
 
 const char* fa_status_string(int status) {

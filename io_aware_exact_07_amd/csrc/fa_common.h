@@ -71,39 +71,80 @@ template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
   return z;
 }
 
-// Column fragment from a row-major LDS tile `base` with row stride `stride`
-// elements.  The lane receives column col0 + (lane % 32) of 8 rows.
+// Row-major LDS tile of D-element rows without padding; 16-byte chunks are
+// XOR-swizzled per row so that both access patterns the kernels use are free
+// of bank conflicts on the 64-bank LDS:
+//   (a) 16 lanes read the same logical chunk of 16 consecutive rows
+//       (row fragments, ds_read_b128);
+//   (b) 32 lanes read 4 consecutive chunks of 4 consecutive rows, rows and
+//       chunks aligned to 4 (column fragments, ds_read_b64_tr_b16).
+// With 128-byte rows (8 chunks) the row's swizzle f takes bits 1..3 of the
+// row so that rows 2 apart differ in bit 2; with >= 256-byte rows it makes
+// the 4 rows of (b) differ in bits 2..3.  Each f is a permutation over 16
+// consecutive rows, which (a) needs.
+template <typename T, int D>
+struct Tile {
+  static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;         // chunks per row
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "unsupported row length");
+  __device__ __forceinline__ static int swz(int row) {
+    return CPR == 8 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+  }
+  // Element offset of (row, col); col % EPC is preserved.
+  __device__ __forceinline__ static int off(int row, int col) {
+    return row * D + ((((col / EPC) ^ swz(row)) * EPC) | (col % EPC));
+  }
+};
+
+// Row fragment: 8 contiguous columns col..col+7 (col a multiple of 8) of one row.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> ld_row_frag(const T* base, int row, int col) {
+  if constexpr (sizeof(T) == 2) {
+    return ld8(base + Tile<T, D>::off(row, col));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(base + Tile<T, D>::off(row, col));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(base + Tile<T, D>::off(row, col + 4));
+    Frag<T> r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
+    return r;
+  }
+}
+
+// Column fragment: the lane receives column col0 + (lane % 32) of 8 rows.
 // PERM = false: register e holds row k0 + 8*h + e               (h = lane/32)
 // PERM = true:  register e holds row k0 + 8*(e/4) + 4*h + e%4
-// The PERM order is the key order in which a 32x32 accumulator's registers
-// 8c..8c+7 enumerate rows 16c..16c+15, so an accumulator can feed a matrix
-// core directly as the contraction operand against this fragment.
-template <bool PERM>
-__device__ __forceinline__ bf16x8 ld_col_frag(const bf16* base, int stride, int k0, int col0, int lane) {
-  const int g = lane >> 4, r = (lane >> 2) & 3, s = lane & 3, h = lane >> 5;
-  const int col = col0 + 16 * (g & 1) + 4 * s;
-  bf16x8 out;
+// The PERM order is the order in which a 32x32 accumulator's registers
+// 8c..8c+7 enumerate its rows 16c..16c+15, so an accumulator converted to T
+// can feed a matrix core directly as the contraction operand against this
+// fragment.
+template <bool PERM, typename T, int D>
+__device__ __forceinline__ Frag<T> ld_col_frag(const T* base, int k0, int col0, int lane) {
+  const int h = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    const int g = lane >> 4, r = (lane >> 2) & 3, s = lane & 3;
+    const int col = col0 + 16 * (g & 1) + 4 * s;
+    bf16x8 out;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = PERM ? (k0 + 8 * t + 4 * h + r) : (k0 + 8 * h + 4 * t + r);
-    const bf16* p = base + row * stride + col;
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-    bf16x4 vb = __builtin_bit_cast(bf16x4, v);
+    for (int t = 0; t < 2; ++t) {
+      const int row = PERM ? (k0 + 8 * t + 4 * h + r) : (k0 + 8 * h + 4 * t + r);
+      const bf16* p = base + Tile<T, D>::off(row, col);
+      s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+      bf16x4 vb = __builtin_bit_cast(bf16x4, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[4 * t + e] = vb[e];
+      for (int e = 0; e < 4; ++e) out[4 * t + e] = vb[e];
+    }
+    return out;
+  } else {
+    const int col = col0 + (lane & 31);
+    f32x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = PERM ? (k0 + 8 * (e >> 2) + 4 * h + (e & 3)) : (k0 + 8 * h + e);
+      out[e] = base[Tile<T, D>::off(row, col)];
+    }
+    return out;
   }
-  return out;
-}
-template <bool PERM>
-__device__ __forceinline__ f32x8 ld_col_frag(const float* base, int stride, int k0, int col0, int lane) {
-  const int h = lane >> 5, col = col0 + (lane & 31);
-  f32x8 out;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = PERM ? (k0 + 8 * (e >> 2) + 4 * h + (e & 3)) : (k0 + 8 * h + e);
-    out[e] = base[row * stride + col];
-  }
-  return out;
 }
 
 // Store 4 consecutive values (converted to T) at p.
@@ -153,13 +194,13 @@ struct TileCopy {
         buf[u] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  template <int STR>
+  // Into a swizzled Tile<T, D> layout.
   __device__ __forceinline__ void store(T* lds, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + u * NT;
       const int row = c / CPR, col = (c % CPR) * EPC;
-      *reinterpret_cast<uint4*>(lds + row * STR + col) = buf[u];
+      *reinterpret_cast<uint4*>(lds + Tile<T, D>::off(row, col)) = buf[u];
     }
   }
 };

@@ -31,16 +31,15 @@ namespace {
 constexpr int kFwdBQ = 128;
 constexpr int kFwdBK = 64;
 constexpr int kFwdThreads = 256;
+constexpr float kSlack = 8.0f;  // probabilities are formed relative to a max at most 2^8 stale
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   constexpr int BQ = kFwdBQ, BK = kFwdBK, NT = kFwdThreads;
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int STR = D + PAD;
   constexpr int NC = D / 16;   // contraction chunks over the head dimension
   constexpr int NDT = D / 32;  // 32-wide output tiles over the head dimension
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * STR];
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * STR];
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];  // swizzled Tile<T, D> layout
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
@@ -85,8 +84,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
   }
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    ck.template store<STR>(sK[buf], tid);
-    cv.template store<STR>(sV[buf], tid);
+    ck.store(sK[buf], tid);
+    cv.store(sV[buf], tid);
     __syncthreads();
     if (kb + 1 < nkb) {
       ck.load(K, (kb + 1) * BK, a.N, tid);
@@ -100,7 +99,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) mma16(s[t], ld8(kt + (t * 32 + n) * STR + 16 * c + 8 * h), qf[c]);
+        for (int c = 0; c < NC; ++c) mma16(s[t], ld_row_frag<T, D>(kt, t * 32 + n, 16 * c + 8 * h), qf[c]);
 
       const bool edge = (k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w);
       if (edge) {
@@ -118,10 +117,21 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
       mx = pair_max(mx);
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_fast((m - mnew) * c2);
-      m = mnew;
-      const float mc = mnew * c2;
+      // The reference max m only moves when some lane's block max exceeds it
+      // by more than kSlack (base-2 units), so exponents stay <= kSlack and
+      // the rescale of the accumulator is skipped for most blocks.  The
+      // result is unchanged: lse and o use the same m consistently.
+      if (__builtin_amdgcn_ballot_w64(mx * c2 > m * c2 + kSlack) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = exp2_fast((m - mnew) * c2);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+      }
+      const float mc = m * c2;
       float rs = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -131,11 +141,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
           s[t][i] = p;
           rs += p;
         }
-      lsum = lsum * alpha + rs;
-#pragma unroll
-      for (int t = 0; t < NDT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+      lsum += rs;
 
       // P^T as contraction operand: chunk c covers keys 16c..16c+15 of the
       // block, registers 8*(c%2)..+7 of tile c/2 (the PERM key order).
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NDT; ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) mma16(acc[t], ld_col_frag<true>(vt, STR, 16 * c, 32 * t, lane), pf[c]);
+        for (int c = 0; c < 4; ++c) mma16(acc[t], ld_col_frag<true, T, D>(vt, 16 * c, 32 * t, lane), pf[c]);
     }
   }
 

@@ -27,7 +27,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;   // float32 [B,H,N,d] scratch
   float* delta;    // float32 [B,H,N] scratch: D_i = dO_i . o_i
   const int32_t* seqlens;
   int B, H, N;
@@ -35,7 +34,9 @@ struct BwdArgs {
 };
 
 // Return hipSuccess or the launch error.  dtype: 0 = bf16, 1 = fp32.
+// The backward pass is three launches: stage 1 = D, stage 2 = dK and dV,
+// stage 3 = dQ.  Stages 2 and 3 each need only stage 1's D.
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_bwd_stage(int stage, const BwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -16,7 +16,7 @@ if not torch.cuda.is_available():
 DEV = "cuda:0"
 
 
-def test_forward_is_bitwise_deterministic():
+def test_forward_and_backward_are_bitwise_deterministic():
     inp = W.random_inputs(2, 3, 700, 64, "bf16", seed=5, gain=2.0)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o1, l1 = fa.forward(q, k, v, causal=True)
@@ -27,8 +27,8 @@ def test_forward_is_bitwise_deterministic():
     g1 = fa.backward(q, k, v, o1, do, l1, causal=True)
     g2 = fa.backward(q, k, v, o1, do, l1, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])  # dK, dV have no atomics
-    assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-2 * g1[0].float().abs().max().item()
+    for a, b in zip(g1, g2):   # no atomics anywhere: every gradient is bitwise reproducible
+        assert torch.equal(a, b)
 
 
 def test_zero_queries_give_prefix_means():

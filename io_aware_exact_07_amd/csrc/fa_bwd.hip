@@ -133,30 +133,39 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   const int qb_begin = CAUSAL ? k0 / BQ : 0;
   const int qb_end = (L + BQ - 1) / BQ;
 
+  // The prefetch keeps the raw loaded values; any arithmetic on them waits
+  // for the load, and the in-order memory counter would then also wait for
+  // the Q and dO tiles issued with it.  They are converted when parked.
   TileCopy<T, BQ, D, NT> cq, cd;
-  float pre_l = 0.f, pre_d = 0.f;
+  float raw_l = 0.f, raw_d = 0.f;
+  int pre_q0 = 0;
   auto fetch = [&](int qb) {
-    const int q0 = qb * BQ;
-    cq.load(Qg, q0, a.N, tid);
-    cd.load(dOg, q0, a.N, tid);
+    pre_q0 = qb * BQ;
+    cq.load(Qg, pre_q0, a.N, tid);
+    cd.load(dOg, pre_q0, a.N, tid);
     if (tid < BQ) {
-      const int qq = q0 + tid;
-      pre_l = qq < L ? LSE[qq] * kLog2e : INFINITY;
-      pre_d = qq < L ? Dv[qq] : 0.f;
+      const int qq = min(pre_q0 + tid, L - 1);  // L >= 1 here
+      raw_l = LSE[qq];
+      raw_d = Dv[qq];
     }
   };
   auto park = [&](int buf) {
     cq.store(sQ[buf], tid);
     cd.store(sdO[buf], tid);
     if (tid < BQ) {
-      sL[buf][tid] = pre_l;
-      sD[buf][tid] = pre_d;
+      const bool in = pre_q0 + tid < L;
+      sL[buf][tid] = in ? raw_l * kLog2e : INFINITY;
+      sD[buf][tid] = in ? raw_d : 0.f;
     }
   };
   if (qb_begin < qb_end) {
     fetch(qb_begin);
     park(0);
   }
+  // Every load issued so far (kf, vf and the first block) has landed; waiting
+  // here lets the loop's matrix products read kf and vf without waiting on
+  // the in-order memory counter, which would also cover the prefetch.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   f32x16 dKacc[NDT], dVacc[NDT];
@@ -173,8 +182,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
     if (more) fetch(qb + 1);
     const T* Qs = sQ[buf];
     const T* dOs = sdO[buf];
-    // Causal: every query of the block is at or past this wave's last key.
-    const bool full = !CAUSAL || q0 >= kw0 + 31;
+    // Masking is needed only where the block crosses the diagonal of this
+    // wave's keys or the wave holds padded keys.
+    const bool edge = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > L);
 
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
@@ -184,6 +194,13 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
         mma16(s, ld_row_frag<T, D>(Qs, 32 * qt + n, 16 * c + 8 * h), kf[c]);
         mma16(dp, ld_row_frag<T, D>(dOs, 32 * qt + n, 16 * c + 8 * h), vf[c]);
       }
+      if (edge) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qq = q0 + 32 * qt + acc_row(i, h);
+          if (!key_ok || (CAUSAL && key > qq)) s[i] = -INFINITY;
+        }
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
@@ -192,11 +209,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * gi + j;
-          const int qq = q0 + 32 * qt + acc_row(i, h);
-          const bool ok = key_ok && (full || key <= qq);
-          const float pv = ok ? exp2_fast(fmaf(s[i], c2, -l4[j])) : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - d4[j]);
+          p[i] = exp2_fast(fmaf(s[i], c2, -l4[j]));
+          ds[i] = p[i] * (dp[i] - d4[j]);
         }
       }
       // Registers 8cc..8cc+7 enumerate queries 16cc..16cc+15 of this tile in
@@ -280,7 +294,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
     qf[c] = (qrow < a.N) ? ld8(Qg + (size_t)qrow * D + 16 * c + 8 * h) : zero_frag<T>();
     df[c] = (qrow < a.N) ? ld8(dOg + (size_t)qrow * D + 16 * c + 8 * h) : zero_frag<T>();
   }
-  const float lse2 = row_ok ? LSE[qrow] * kLog2e : 0.f;
+  // Rows past L get lse = +inf (every probability 0) and D = 0.
+  const float lse2 = row_ok ? LSE[qrow] * kLog2e : INFINITY;
   const float dq_i = row_ok ? Dv[qrow] : 0.f;
   const float c2 = a.scale * kLog2e;
 
@@ -315,15 +330,23 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
           mma16(s[t], ld_row_frag<T, D>(kt, t * 32 + n, 16 * c + 8 * h), qf[c]);
           mma16(dp[t], ld_row_frag<T, D>(vt, t * 32 + n, 16 * c + 8 * h), df[c]);
         }
-      const bool edge = (k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w);
+      // Masked scores become -inf (probability exactly 0); only blocks that
+      // cross the padding boundary or the diagonal take this branch.
+      if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * t + acc_row(i, h);
+            if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
+          }
+      }
       Frag<T> dsf[4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * t + acc_row(i, h);
-          const bool ok = row_ok && (!edge || (key < L && (!CAUSAL || key <= qrow)));
-          const float p = ok ? exp2_fast(fmaf(s[t][i], c2, -lse2)) : 0.f;
+          const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
           dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] - dq_i));
         }
 #pragma unroll

@@ -29,6 +29,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unconstrained
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct FragOf;

@@ -155,7 +155,7 @@ def main():
         st = fa.fa_fwd(P[0], P[1], P[2], P[3], P[4], B, H, N, d, scale, 1, None, fa.FA_BF16, sp)
         if ev is not None:
             ev[0].record(stream)
-        st |= fa.fa_bwd_prepare(P[3], P[8], B, H, N, d, None, P[9], wsb, fa.FA_BF16, sp)
+        st |= fa.fa_bwd_prepare(P[3], P[8], P[4], B, H, N, d, None, P[9], wsb, fa.FA_BF16, sp)
         if ev is not None:
             ev[1].record(stream)
         st |= fa.fa_bwd_dkdv(P[0], P[1], P[2], P[8], P[4], P[6], P[7], B, H, N, d, scale, 1, None, P[9], wsb,

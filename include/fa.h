@@ -74,9 +74,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* seqlens, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the float32 row vector
- * D [B,H,N] (D_i = dO_i . o_i), rounded up to 256 bytes.  Linear in N.
- * Returns 0 for empty or invalid shapes.
+ * Bytes of device workspace fa_bwd needs: two float32 row vectors per head,
+ * D_i = dO_i . o_i and lse_i * log2(e), each holding N rounded up to a
+ * multiple of 128 rows per head (the padding rows are written too), each
+ * rounded up to 256 bytes.  Linear in N.  Returns 0 for empty or invalid
+ * shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
@@ -100,9 +102,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * separately or run the two gradient stages concurrently.  Calling prepare,
  * then dkdv and dq (in either order, or on two streams ordered after
  * prepare) with one workspace is exactly fa_bwd.
- *   prepare: D_i = dO_i . o_i into the workspace (reads o, dO).  A row of
- *            the softmax-Jacobian product reduces to dS_ij = P_ij (dP_ij - D_i)
- *            because sum_j P_ij dP_ij = dO_i . o_i.
+ *   prepare: D_i = dO_i . o_i and lse_i in base 2 into the workspace (reads
+ *            o, dO, lse).  A row of the softmax-Jacobian product reduces to
+ *            dS_ij = P_ij (dP_ij - D_i) because sum_j P_ij dP_ij = dO_i . o_i.
  *   dkdv:    recomputes the score blocks key block by key block and writes
  *            dk and dv (reads q, k, v, dO, lse and the prepared workspace).
  *   dq:      recomputes the score blocks query block by query block and
@@ -110,8 +112,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */
-int fa_bwd_prepare(const void* o, const void* dO, int B, int H, int N, int d,
-                   const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+int fa_bwd_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N,
+                   int d, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
                    int dtype, void* stream);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                 const float* lse, void* dk, void* dv, int B, int H, int N, int d,

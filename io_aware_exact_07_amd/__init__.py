@@ -52,7 +52,7 @@ def lib():
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
         L.fa_bwd.restype = ci
-        L.fa_bwd_prepare.argtypes = [vp, vp, ci, ci, ci, ci, vp, vp, sz, ci, vp]
+        L.fa_bwd_prepare.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, vp, sz, ci, vp]
         L.fa_bwd_prepare.restype = ci
         L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
         L.fa_bwd_dkdv.restype = ci
@@ -76,8 +76,8 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, 
                         workspace, workspace_bytes, dtype, stream)
 
 
-def fa_bwd_prepare(o, dO, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream) -> int:
-    return lib().fa_bwd_prepare(o, dO, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream)
+def fa_bwd_prepare(o, dO, lse, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream) -> int:
+    return lib().fa_bwd_prepare(o, dO, lse, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream)
 
 
 def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, scale, causal, seqlens, workspace, workspace_bytes,

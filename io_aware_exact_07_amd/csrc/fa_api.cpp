@@ -51,7 +51,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   int st = check_common(B, H, N, d, 1.0f, dtype);
   if (st != FA_OK) return 0;
-  return round_up((size_t)B * H * N * sizeof(float), 256);
+  return 2 * round_up((size_t)B * H * fa::padded_rows(N) * sizeof(float), 256);
 }
 
 namespace {
@@ -66,7 +66,8 @@ int bwd_setup(const void* q, const void* k, const void* v, const void* o, const 
   if (st != FA_OK) return st;
   const bool compute = stage == kAll || stage == kDkDv || stage == kDq;
   if (compute && (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v))) return FA_ERR_INVALID_ARG;
-  if ((stage == kAll || stage == kPrepare) && !tensor_ok(o)) return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kPrepare) && (!tensor_ok(o) || lse == nullptr || !aligned(lse, 4)))
+    return FA_ERR_INVALID_ARG;
   if (!tensor_ok(dO)) return FA_ERR_INVALID_ARG;
   if ((stage == kAll || stage == kDkDv) && (!tensor_ok(dk) || !tensor_ok(dv))) return FA_ERR_INVALID_ARG;
   if ((stage == kAll || stage == kDq) && !tensor_ok(dq)) return FA_ERR_INVALID_ARG;
@@ -74,7 +75,9 @@ int bwd_setup(const void* q, const void* k, const void* v, const void* o, const 
   if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
   if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  *a = fa::BwdArgs{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), seqlens, B, H, N, scale};
+  float* lse2 = static_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  *a = fa::BwdArgs{q, k, v, o, dO, lse, dq, dk, dv, lse2, delta, seqlens, B, H, N, scale};
   return FA_OK;
 }
 
@@ -102,10 +105,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return run_stages(kPrepare, kDq, a, d, dtype, causal, stream);
 }
 
-int fa_bwd_prepare(const void* o, const void* dO, int B, int H, int N, int d, const int32_t* seqlens,
-                   void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+int fa_bwd_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                   const int32_t* seqlens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   fa::BwdArgs a;
-  int st = bwd_setup(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr, B, H, N, d, 1.0f, seqlens,
+  int st = bwd_setup(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr, B, H, N, d, 1.0f, seqlens,
                      workspace, workspace_bytes, dtype, kPrepare, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;

@@ -22,6 +22,8 @@
 // at 4 bytes per (key block, query, dim) their request rate, not the two
 // extra matrix products per score block, bounds the pass.  Stages 2 and 3
 // are independent once D exists.  Everything is deterministic.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -32,12 +34,17 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// 1. D_i = dO_i . o_i.  CPR threads cooperate on one row.
+// 1. Row vectors for the gradient stages, over Npad rows per head:
+//    delta[i] = dO_i . o_i and lse2[i] = lse_i * log2(e) for rows i < L;
+//    delta = 0 and lse2 = +inf (every probability of the row 0) for padded
+//    rows and for the rows that round the head up to whole 128-row blocks.
+//    CPR threads cooperate on one row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int CPR = D / EPC;  // 16-byte chunks per row: 8, 16 or 32
-  const long long rows = (long long)a.B * a.H * a.N;
+  const int Np = padded_rows(a.N);
+  const long long rows = (long long)a.B * a.H * Np;
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
   const T* O = reinterpret_cast<const T*>(a.o);
@@ -45,11 +52,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   // Every thread of a row group runs the same trip count, so the shuffles
   // below always see all CPR lanes of the group.
   for (long long t = gtid; t < ((rows * CPR + stride - 1) / stride) * stride; t += stride) {
-    const long long row = t / CPR;
+    const long long prow = t / CPR;  // row in the padded layout
     const int part = (int)(t % CPR);
+    const long long bh = prow / Np;
+    const int pos = (int)(prow % Np);
+    const int L = prow < rows ? clamp_len(a.seqlens, (int)(bh / a.H), a.N) : 0;
+    const bool in = prow < rows && pos < L;
     float dot = 0.f;
-    const bool in = row < rows;
     if (in) {
+      const long long row = bh * a.N + pos;
       const uint4 ov = *reinterpret_cast<const uint4*>(O + row * D + part * EPC);
       const uint4 dv = *reinterpret_cast<const uint4*>(dO + row * D + part * EPC);
       const T* op = reinterpret_cast<const T*>(&ov);
@@ -59,11 +70,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, CPR);
-    if (in && part == 0) {
-      const int pos = (int)(row % a.N);
-      const int b = (int)(row / ((long long)a.H * a.N));
-      const int L = clamp_len(a.seqlens, b, a.N);
-      a.delta[row] = pos < L ? dot : 0.f;
+    if (prow < rows && part == 0) {
+      a.delta[prow] = in ? dot : 0.f;
+      a.lse2[prow] = in ? a.lse[bh * a.N + pos] * kLog2e : INFINITY;
     }
   }
 }
@@ -83,10 +92,34 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   constexpr int NC = D / 16;
   constexpr int NDT = D / 32;
   constexpr int NQT = BQ / 32;
-  __shared__ __attribute__((aligned(16))) T sQ[2][BQ * D];   // swizzled Tile<T, D>
-  __shared__ __attribute__((aligned(16))) T sdO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];  // lse * log2(e); +inf for rows >= L
-  __shared__ __attribute__((aligned(16))) float sD[2][BQ];  // D_i; 0 for rows >= L
+  // Three pipeline stages, each its own LDS arrays: Q and dO tiles (swizzled
+  // Tile<T, D>) and the block's lse2 | D row vectors, filled by direct
+  // HBM -> LDS copies issued two blocks ahead.
+  constexpr int S = 3;
+  __shared__ __attribute__((aligned(16))) T sQ0[BQ * D];
+  __shared__ __attribute__((aligned(16))) T sO0[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sR0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) T sQ1[BQ * D];
+  __shared__ __attribute__((aligned(16))) T sO1[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sR1[2 * BQ];
+  __shared__ __attribute__((aligned(16))) T sQ2[BQ * D];
+  __shared__ __attribute__((aligned(16))) T sO2[BQ * D];
+  __shared__ __attribute__((aligned(16))) float sR2[2 * BQ];
+  auto qst = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sQ0;
+    else if constexpr (decltype(STG)::value == 1) return sQ1;
+    else return sQ2;
+  };
+  auto ost = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sO0;
+    else if constexpr (decltype(STG)::value == 1) return sO1;
+    else return sO2;
+  };
+  auto rst = [&](auto STG) -> float* {
+    if constexpr (decltype(STG)::value == 0) return sR0;
+    else if constexpr (decltype(STG)::value == 1) return sR1;
+    else return sR2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
@@ -101,8 +134,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   const T* dOg = reinterpret_cast<const T*>(a.dO) + hoff;
   T* dKg = reinterpret_cast<T*>(a.dk) + hoff;
   T* dVg = reinterpret_cast<T*>(a.dv) + hoff;
-  const float* LSE = a.lse + (size_t)bh * a.N;
-  const float* Dv = a.delta + (size_t)bh * a.N;
+  const size_t roff = (size_t)bh * padded_rows(a.N);
+  const float* L2g = a.lse2 + roff;
+  const float* Dg = a.delta + roff;
 
   const int k0 = kb * BK;
   const int kw0 = k0 + 32 * w;  // this wave's first key
@@ -128,45 +162,31 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
     kf[c] = key < a.N ? ld8(Kg + (size_t)key * D + 16 * c + 8 * h) : zero_frag<T>();
     vf[c] = key < a.N ? ld8(Vg + (size_t)key * D + 16 * c + 8 * h) : zero_frag<T>();
   }
+  // Every load so far has landed; the loop's matrix products then never wait
+  // on the in-order memory counter for kf and vf.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const float c2 = a.scale * kLog2e;
   const int qb_begin = CAUSAL ? k0 / BQ : 0;
   const int qb_end = (L + BQ - 1) / BQ;
 
-  // The prefetch keeps the raw loaded values; any arithmetic on them waits
-  // for the load, and the in-order memory counter would then also wait for
-  // the Q and dO tiles issued with it.  They are converted when parked.
-  TileCopy<T, BQ, D, NT> cq, cd;
-  float raw_l = 0.f, raw_d = 0.f;
-  int pre_q0 = 0;
-  auto fetch = [&](int qb) {
-    pre_q0 = qb * BQ;
-    cq.load(Qg, pre_q0, a.N, tid);
-    cd.load(dOg, pre_q0, a.N, tid);
-    if (tid < BQ) {
-      const int qq = min(pre_q0 + tid, L - 1);  // L >= 1 here
-      raw_l = LSE[qq];
-      raw_d = Dv[qq];
+  TileDma<T, BQ, D, NT> dma;
+  dma.init(tid);
+  // Wave 0 also copies the row vectors: lanes [0, BQ/4) take lse2, lanes
+  // [BQ/4, BQ/2) take D, into one 2*BQ-float stage array.
+  constexpr int VM_OTHERS = 2 * TileDma<T, BQ, D, NT>::PER;
+  constexpr int VM_WAVE0 = VM_OTHERS + 1;
+  auto issue = [&](int qb, auto STG) {
+    const int q0 = qb * BQ;
+    dma.issue(Qg, q0, a.N, qst(STG), tid);
+    dma.issue(dOg, q0, a.N, ost(STG), tid);
+    if (w == 0 && lane < BQ / 2) {
+      const float* src = lane < BQ / 4 ? L2g + q0 + 4 * lane : Dg + q0 + 4 * (lane - BQ / 4);
+      dma16(src, rst(STG));
     }
   };
-  auto park = [&](int buf) {
-    cq.store(sQ[buf], tid);
-    cd.store(sdO[buf], tid);
-    if (tid < BQ) {
-      const bool in = pre_q0 + tid < L;
-      sL[buf][tid] = in ? raw_l * kLog2e : INFINITY;
-      sD[buf][tid] = in ? raw_d : 0.f;
-    }
-  };
-  if (qb_begin < qb_end) {
-    fetch(qb_begin);
-    park(0);
-  }
-  // Every load issued so far (kf, vf and the first block) has landed; waiting
-  // here lets the loop's matrix products read kf and vf without waiting on
-  // the in-order memory counter, which would also cover the prefetch.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
+  if (qb_begin < qb_end) issue(qb_begin, std::integral_constant<int, 0>());
+  if (qb_begin + 1 < qb_end) issue(qb_begin + 1, std::integral_constant<int, 1>());
 
   f32x16 dKacc[NDT], dVacc[NDT];
 #pragma unroll
@@ -175,15 +195,29 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
     dVacc[t] = zero16();
   }
 
-  for (int qb = qb_begin; qb < qb_end; ++qb) {
-    const int buf = (qb - qb_begin) & 1;
+  FragAddr<T, D> fr;
+  fr.init(lane);
+  // One query block from pipeline stage STG (compile-time, so every LDS
+  // address is a precomputed per-lane offset plus an immediate).
+  auto block = [&](const int qb, auto STG) {
+    constexpr int buf = decltype(STG)::value;
+    constexpr int nxt = (buf + S - 1) % S;
+    // Block qb has landed once at most the next block's copies are pending.
+    if (qb + 1 < qb_end) {
+      if (w == 0) __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_WAVE0));
+      else __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_OTHERS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+    }
+    barrier_lds();  // block qb visible to all waves; stage nxt no longer read
+    if (qb + 2 < qb_end) issue(qb + 2, std::integral_constant<int, nxt>());
     const int q0 = qb * BQ;
-    const bool more = qb + 1 < qb_end;
-    if (more) fetch(qb + 1);
-    const T* Qs = sQ[buf];
-    const T* dOs = sdO[buf];
+    const T* Qs = qst(STG);
+    const T* dOs = ost(STG);
+    const float* Rs = rst(STG);
     // Masking is needed only where the block crosses the diagonal of this
-    // wave's keys or the wave holds padded keys.
+    // wave's keys or the wave holds padded keys (padded query rows carry
+    // lse2 = +inf and D = 0).
     const bool edge = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > L);
 
 #pragma unroll
@@ -191,8 +225,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        mma16(s, ld_row_frag<T, D>(Qs, 32 * qt + n, 16 * c + 8 * h), kf[c]);
-        mma16(dp, ld_row_frag<T, D>(dOs, 32 * qt + n, 16 * c + 8 * h), vf[c]);
+        mma16(s, fr.row(Qs, qt, c), kf[c]);
+        mma16(dp, fr.row(dOs, qt, c), vf[c]);
       }
       if (edge) {
 #pragma unroll
@@ -204,8 +238,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
       float p[16], ds[16];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qt + 8 * gi + 4 * h]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qt + 8 * gi + 4 * h]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Rs + 32 * qt + 8 * gi + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Rs + BQ + 32 * qt + 8 * gi + 4 * h);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * gi + j;
@@ -227,12 +261,15 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
       for (int t = 0; t < NDT; ++t)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          mma16(dVacc[t], pf[cc], ld_col_frag<true, T, D>(dOs, 32 * qt + 16 * cc, 32 * t, lane));
-          mma16(dKacc[t], dsf[cc], ld_col_frag<true, T, D>(Qs, 32 * qt + 16 * cc, 32 * t, lane));
+          mma16(dVacc[t], pf[cc], fr.col(dOs, 32 * qt + 16 * cc, t));
+          mma16(dKacc[t], dsf[cc], fr.col(Qs, 32 * qt + 16 * cc, t));
         }
     }
-    if (more) park(buf ^ 1);
-    __syncthreads();  // the next query block is in LDS; this one is no longer read
+  };
+  for (int qb = qb_begin; qb < qb_end; qb += S) {
+    block(qb, std::integral_constant<int, 0>());
+    if (qb + 1 < qb_end) block(qb + 1, std::integral_constant<int, 1>());
+    if (qb + 2 < qb_end) block(qb + 2, std::integral_constant<int, 2>());
   }
 
   // dV / dK tiles: lane = head-dim column, registers = keys.
@@ -260,8 +297,26 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   constexpr int BQ = 128, BK = 64, NT = kThreads;
   constexpr int NC = D / 16;
   constexpr int NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];  // swizzled Tile<T, D>
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+  // Pipeline stages as in the forward kernel: K/V blocks copied HBM -> LDS
+  // S-1 blocks ahead, each stage its own LDS arrays.
+  constexpr int S = (sizeof(T) == 2 && D == 64) ? 3 : 2;
+  constexpr int TS = BK * D, TS2 = S > 2 ? BK * D : 8;
+  __shared__ __attribute__((aligned(16))) T sK0[TS];  // swizzled Tile<T, D>
+  __shared__ __attribute__((aligned(16))) T sV0[TS];
+  __shared__ __attribute__((aligned(16))) T sK1[TS];
+  __shared__ __attribute__((aligned(16))) T sV1[TS];
+  __shared__ __attribute__((aligned(16))) T sK2[TS2];
+  __shared__ __attribute__((aligned(16))) T sV2[TS2];
+  auto kst = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sK0;
+    else if constexpr (decltype(STG)::value == 1) return sK1;
+    else return sK2;
+  };
+  auto vst = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sV0;
+    else if constexpr (decltype(STG)::value == 1) return sV1;
+    else return sV2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
@@ -276,8 +331,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   const T* Vg = reinterpret_cast<const T*>(a.v) + hoff;
   const T* dOg = reinterpret_cast<const T*>(a.dO) + hoff;
   T* dQg = reinterpret_cast<T*>(a.dq) + hoff;
-  const float* LSE = a.lse + (size_t)bh * a.N;
-  const float* Dv = a.delta + (size_t)bh * a.N;
+  const size_t roff = (size_t)bh * padded_rows(a.N);
 
   const int q0w = qb * BQ + w * 32;
   const int qrow = q0w + n;
@@ -294,65 +348,82 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
     qf[c] = (qrow < a.N) ? ld8(Qg + (size_t)qrow * D + 16 * c + 8 * h) : zero_frag<T>();
     df[c] = (qrow < a.N) ? ld8(dOg + (size_t)qrow * D + 16 * c + 8 * h) : zero_frag<T>();
   }
-  // Rows past L get lse = +inf (every probability 0) and D = 0.
-  const float lse2 = row_ok ? LSE[qrow] * kLog2e : INFINITY;
-  const float dq_i = row_ok ? Dv[qrow] : 0.f;
+  // Padded and past-the-end rows carry lse2 = +inf (every probability 0), D = 0.
+  const float lse2 = a.lse2[roff + qrow];
+  const float dq_i = a.delta[roff + qrow];
   const float c2 = a.scale * kLog2e;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = zero16();
 
   const int nkb = (kend + BK - 1) / BK;
-  TileCopy<T, BK, D, NT> ck, cv;
-  if (nkb > 0) {
-    ck.load(Kg, 0, a.N, tid);
-    cv.load(Vg, 0, a.N, tid);
+  FragAddr<T, D> fr;
+  fr.init(lane);
+  TileDma<T, BK, D, NT> dma;
+  dma.init(tid);
+  constexpr int VM_PER_BLOCK = 2 * TileDma<T, BK, D, NT>::PER;
+  auto issue = [&](int kb, T* kd, T* vd) {
+    dma.issue(Kg, kb * BK, a.N, kd, tid);
+    dma.issue(Vg, kb * BK, a.N, vd, tid);
+  };
+  if (0 < nkb) issue(0, sK0, sV0);
+  if constexpr (S > 2) {
+    if (1 < nkb) issue(1, sK1, sV1);
   }
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    ck.store(sK[buf], tid);
-    cv.store(sV[buf], tid);
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      ck.load(Kg, (kb + 1) * BK, a.N, tid);
-      cv.load(Vg, (kb + 1) * BK, a.N, tid);
-    }
+  // One key/value block from pipeline stage STG (compile-time, so every LDS
+  // address is a precomputed per-lane offset plus an immediate).
+  auto block = [&](const int kb, auto STG) {
+    constexpr int buf = decltype(STG)::value;
+    constexpr int nxt = (buf + S - 1) % S;
+    if (kb + S - 2 < nkb)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_PER_BLOCK * (S - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+    barrier_lds();  // block kb visible to all waves; stage nxt no longer read
+    if (kb + S - 1 < nkb) issue(kb + S - 1, kst(std::integral_constant<int, nxt>()), vst(std::integral_constant<int, nxt>()));
     const int k0 = kb * BK;
-    if (wave_live && k0 < kend_w) {
-      const T* kt = sK[buf];
-      const T* vt = sV[buf];
-      f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+    if (!(wave_live && k0 < kend_w)) return;
+    const T* kt = kst(STG);
+    const T* vt = vst(STG);
+    f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          mma16(s[t], ld_row_frag<T, D>(kt, t * 32 + n, 16 * c + 8 * h), qf[c]);
-          mma16(dp[t], ld_row_frag<T, D>(vt, t * 32 + n, 16 * c + 8 * h), df[c]);
-        }
-      // Masked scores become -inf (probability exactly 0); only blocks that
-      // cross the padding boundary or the diagonal take this branch.
-      if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * t + acc_row(i, h);
-            if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
-          }
+      for (int c = 0; c < NC; ++c) {
+        mma16(s[t], fr.row(kt, t, c), qf[c]);
+        mma16(dp[t], fr.row(vt, t, c), df[c]);
       }
-      Frag<T> dsf[4];
+    // Masked scores become -inf (probability exactly 0); only blocks that
+    // cross the padding boundary or the diagonal take this branch.
+    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
-          dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] - dq_i));
+          const int key = k0 + 32 * t + acc_row(i, h);
+          if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
         }
+    }
+    Frag<T> dsf[4];
 #pragma unroll
-      for (int t = 0; t < NDT; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) mma16(acc[t], ld_col_frag<true, T, D>(kt, 16 * c, 32 * t, lane), dsf[c]);
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
+        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] - dq_i));
+      }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mma16(acc[t], fr.col(kt, 16 * c, t), dsf[c]);
+  };
+  for (int kb = 0; kb < nkb; kb += S) {
+    block(kb, std::integral_constant<int, 0>());
+    if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>());
+    if constexpr (S > 2) {
+      if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>());
     }
   }
 
@@ -376,7 +447,7 @@ unsigned grid_for(long long work, int threads) {
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_one(int stage, const BwdArgs& a, hipStream_t stream) {
   constexpr int CPR = D * (int)sizeof(T) / 16;
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = (long long)a.B * a.H * padded_rows(a.N);
   if (stage == 1) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid_for(rows * CPR, 256)), dim3(256), 0, stream, a);
   } else {

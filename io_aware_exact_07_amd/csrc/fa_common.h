@@ -150,6 +150,65 @@ __device__ __forceinline__ Frag<T> ld_col_frag(const T* base, int k0, int col0, 
   }
 }
 
+// Per-lane element offsets of every fragment a kernel reads from a Tile<T, D>,
+// computed once.  The parts of a fragment address that vary inside the loops
+// (the 32-row tile index of a row fragment, the 16-row block of a column
+// fragment, the double-buffer slot) are multiples of whole rows, which the
+// swizzle does not see, so they stay compile-time immediates of the LDS
+// instructions.
+//   row(base, r32, c): row fragment of row 32*r32 + (lane % 32), columns
+//                      16c + 8h .. +7 (h = lane / 32)
+//   col(base, k0, dt): PERM column fragment of rows k0.. (k0 a multiple of
+//                      16), columns 32*dt + (lane % 32)
+template <typename T, int D>
+struct FragAddr;
+
+template <int D>
+struct FragAddr<bf16, D> {
+  using TL = Tile<bf16, D>;
+  static constexpr int NC = D / 16, NDT = D / 32;
+  int rofs[NC];
+  int cofs[2][NDT];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, n = lane & 31;
+    const int g = lane >> 4, r = (lane >> 2) & 3, s = lane & 3;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) rofs[c] = TL::off(n, 16 * c + 8 * h);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) cofs[t][dt] = TL::off(8 * t + 4 * h + r, 32 * dt + 16 * (g & 1) + 4 * s);
+  }
+  __device__ __forceinline__ bf16x8 row(const bf16* base, int r32, int c) const {
+    return ld8(base + rofs[c] + 32 * r32 * D);
+  }
+  __device__ __forceinline__ bf16x8 col(const bf16* base, int k0, int dt) const {
+    bf16x8 out;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16* p = base + cofs[t][dt] + k0 * D;
+      s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+      bf16x4 vb = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[4 * t + e] = vb[e];
+    }
+    return out;
+  }
+};
+
+// fp32 (parity path): addresses computed at each use.
+template <int D>
+struct FragAddr<float, D> {
+  int lane_;
+  __device__ __forceinline__ void init(int lane) { lane_ = lane; }
+  __device__ __forceinline__ f32x8 row(const float* base, int r32, int c) const {
+    return ld_row_frag<float, D>(base, 32 * r32 + (lane_ & 31), 16 * c + 8 * (lane_ >> 5));
+  }
+  __device__ __forceinline__ f32x8 col(const float* base, int k0, int dt) const {
+    return ld_col_frag<true, float, D>(base, k0, 32 * dt, lane_);
+  }
+};
+
 // Store 4 consecutive values (converted to T) at p.
 __device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v;
@@ -207,6 +266,91 @@ struct TileCopy {
     }
   }
 };
+
+// One global_load_lds_dwordx4: every active lane copies 16 bytes from its
+// `src` to dst + 16 * lane, where dst (wave-uniform) goes in M0.  Issued
+// through asm so that the compiler's LDS-DMA tracking, which cannot tell the
+// pipeline stages apart and would wait for every copy in flight before any
+// LDS read, stays out; callers wait with explicit vmcnt before a barrier.
+// M0 is reserved to the compiler, which on gfx950 sets it only right before
+// the few instructions that read it (none of which these kernels use), so
+// overwriting it here is safe; the clobber entry documents it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(dst));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(m0), "v"(src)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Direct HBM -> LDS copy (global_load_lds_dwordx4) of rows [r0, r0+R) of a
+// row-major [nrows][D] array into a swizzled Tile<T, D>.  Each instruction
+// moves 64 lanes x 16 bytes into a contiguous 1 KB span of LDS (lane l
+// writes bytes 16l..16l+15 of the span), so lane l of wave w, instruction u,
+// fills physical chunk P = (u*NW + w)*64 + l and loads the global chunk that
+// the swizzle maps there.  Rows >= nrows re-read row nrows-1 (finite data the
+// kernels mask out).  Completion is tracked by the wave's vmcnt; the data is
+// visible to other waves after a workgroup barrier.
+template <typename T, int R, int D, int NT>
+struct TileDma {
+  static constexpr int EPC = 16 / sizeof(T);
+  static constexpr int CPR = D / EPC;
+  static constexpr int NW = NT / 64;
+  static constexpr int TOTAL = R * CPR;
+  static_assert(TOTAL % NT == 0, "tile must split evenly over the threads");
+  static constexpr int PER = TOTAL / NT;  // instructions per thread per tile
+  int gofs[PER];                          // element offset of this lane's chunk in rows r0..
+  int prow[PER];                          // tile row of that chunk
+  __device__ __forceinline__ void init(int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int P = (u * NW + w) * 64 + lane;
+      const int row = P / CPR, pc = P % CPR;
+      prow[u] = row;
+      gofs[u] = row * D + (pc ^ Tile<T, D>::swz(row)) * EPC;
+    }
+  }
+  __device__ __forceinline__ void issue(const T* g, int r0, int nrows, T* lds, int tid) const {
+    const int w = tid >> 6;
+    const bool inside = r0 + R <= nrows;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const T* src;
+      if (inside) {
+        src = g + (size_t)r0 * D + gofs[u];
+      } else {
+        const int gr = min(r0 + prow[u], nrows - 1);
+        src = g + (size_t)gr * D + (gofs[u] - prow[u] * D);
+      }
+      T* dst = lds + (u * NW + w) * 64 * EPC;
+      dma16(src, dst);
+    }
+  }
+};
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// instructions (lgkmcnt(0)) but not for its outstanding global loads, so
+// direct-to-LDS copies of later pipeline stages stay in flight across it.
+// (A fenced barrier would also wait for every outstanding LDS DMA.)  The
+// empty asm statements keep the compiler from moving memory accesses across.
+// Callers wait for the DMA a stage needs with an explicit vmcnt before it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate for vmcnt(n) (n < 64) with expcnt and lgkmcnt unconstrained.
+__device__ __forceinline__ constexpr int wait_vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
   if (!seqlens) return N;

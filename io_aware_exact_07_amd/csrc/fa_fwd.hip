@@ -21,6 +21,8 @@
 // backward pass needs besides Q, K, V, O (Brenndoerfer, "FlashAttention
 // Algorithm > Recomputation Strategy", "What Gets Stored vs Recomputed": the
 // running max m and normaliser L; stored here as their combination).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -38,8 +40,28 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   constexpr int BQ = kFwdBQ, BK = kFwdBK, NT = kFwdThreads;
   constexpr int NC = D / 16;   // contraction chunks over the head dimension
   constexpr int NDT = D / 32;  // 32-wide output tiles over the head dimension
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];  // swizzled Tile<T, D> layout
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+  // Pipeline depth: blocks kb+1 .. kb+S-1 are in flight while block kb is
+  // computed, which covers the HBM/L2 round trip at d=64.
+  // Each stage is its own LDS array so the compiler can tell that copies
+  // into one stage never alias reads of another.
+  constexpr int S = (sizeof(T) == 2 && D == 64) ? 3 : 2;
+  constexpr int TS = BK * D, TS2 = S > 2 ? BK * D : 8;
+  __shared__ __attribute__((aligned(16))) T sK0[TS];  // swizzled Tile<T, D> layout
+  __shared__ __attribute__((aligned(16))) T sV0[TS];
+  __shared__ __attribute__((aligned(16))) T sK1[TS];
+  __shared__ __attribute__((aligned(16))) T sV1[TS];
+  __shared__ __attribute__((aligned(16))) T sK2[TS2];
+  __shared__ __attribute__((aligned(16))) T sV2[TS2];
+  auto kst = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sK0;
+    else if constexpr (decltype(STG)::value == 1) return sK1;
+    else return sK2;
+  };
+  auto vst = [&](auto STG) -> T* {
+    if constexpr (decltype(STG)::value == 0) return sV0;
+    else if constexpr (decltype(STG)::value == 1) return sV1;
+    else return sV2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
@@ -76,84 +98,103 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   float lsum = 0.f;   // this lane's half of the running normaliser
   const float c2 = a.scale * kLog2e;
 
+  // The query fragments have landed before any copy is issued, so the loop's
+  // matrix products never wait on the in-order memory counter for them.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const int nkb = (kend + BK - 1) / BK;
-  TileCopy<T, BK, D, NT> ck, cv;
-  if (nkb > 0) {
-    ck.load(K, 0, a.N, tid);
-    cv.load(V, 0, a.N, tid);
+  FragAddr<T, D> fr;
+  fr.init(lane);
+  TileDma<T, BK, D, NT> dma;
+  dma.init(tid);
+  constexpr int VM_PER_BLOCK = 2 * TileDma<T, BK, D, NT>::PER;
+  auto issue = [&](int kb, T* kd, T* vd) {
+    dma.issue(K, kb * BK, a.N, kd, tid);
+    dma.issue(V, kb * BK, a.N, vd, tid);
+  };
+  if (0 < nkb) issue(0, sK0, sV0);
+  if constexpr (S > 2) {
+    if (1 < nkb) issue(1, sK1, sV1);
   }
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    ck.store(sK[buf], tid);
-    cv.store(sV[buf], tid);
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      ck.load(K, (kb + 1) * BK, a.N, tid);
-      cv.load(V, (kb + 1) * BK, a.N, tid);
-    }
+  // One key/value block from pipeline stage STG (compile-time, so every LDS
+  // address below is a precomputed per-lane offset plus an immediate).
+  auto block = [&](const int kb, auto STG) {
+    constexpr int buf = decltype(STG)::value;
+    constexpr int nxt = (buf + S - 1) % S;
+    // Block kb has landed once at most the later blocks' copies are pending.
+    if (kb + S - 2 < nkb)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_PER_BLOCK * (S - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+    barrier_lds();  // block kb visible to all waves; stage nxt no longer read
+    if (kb + S - 1 < nkb) issue(kb + S - 1, kst(std::integral_constant<int, nxt>()), vst(std::integral_constant<int, nxt>()));
     const int k0 = kb * BK;
-    if (wave_live && k0 < kend_w) {
-      const T* kt = sK[buf];
-      const T* vt = sV[buf];
-      f32x16 s[2] = {zero16(), zero16()};
+    if (!(wave_live && k0 < kend_w)) return;
+    const T* kt = kst(STG);
+    const T* vt = vst(STG);
+    f32x16 s[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) mma16(s[t], ld_row_frag<T, D>(kt, t * 32 + n, 16 * c + 8 * h), qf[c]);
+      for (int c = 0; c < NC; ++c) mma16(s[t], fr.row(kt, t, c), qf[c]);
 
-      const bool edge = (k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w);
-      if (edge) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * t + acc_row(i, h);
-            if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
-      mx = pair_max(mx);
-      // The reference max m only moves when some lane's block max exceeds it
-      // by more than kSlack (base-2 units), so exponents stay <= kSlack and
-      // the rescale of the accumulator is skipped for most blocks.  The
-      // result is unchanged: lse and o use the same m consistently.
-      if (__builtin_amdgcn_ballot_w64(mx * c2 > m * c2 + kSlack) != 0) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = exp2_fast((m - mnew) * c2);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
-      }
-      const float mc = m * c2;
-      float rs = 0.f;
+    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(fmaf(s[t][i], c2, -mc));
-          s[t][i] = p;
-          rs += p;
+          const int key = k0 + 32 * t + acc_row(i, h);
+          if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
         }
-      lsum += rs;
-
-      // P^T as contraction operand: chunk c covers keys 16c..16c+15 of the
-      // block, registers 8*(c%2)..+7 of tile c/2 (the PERM key order).
-      Frag<T> pf[4];
+    }
+    float mx = s[0][0];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[c][e] = (T)s[c >> 1][8 * (c & 1) + e];
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[t][i]);
+    mx = pair_max(mx);
+    // The reference max m only moves when some lane's block max exceeds it
+    // by more than kSlack (base-2 units), so exponents stay <= kSlack and
+    // the rescale of the accumulator is skipped for most blocks.  The
+    // result is unchanged: lse and o use the same m consistently.
+    if (__builtin_amdgcn_ballot_w64(mx * c2 > m * c2 + kSlack) != 0) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_fast((m - mnew) * c2);
+      m = mnew;
+      lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < NDT; ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) mma16(acc[t], ld_col_frag<true, T, D>(vt, 16 * c, 32 * t, lane), pf[c]);
+        for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+    }
+    const float mc = m * c2;
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(fmaf(s[t][i], c2, -mc));
+        s[t][i] = p;
+        rs += p;
+      }
+    lsum += rs;
+
+    // P^T as contraction operand: chunk c covers keys 16c..16c+15 of the
+    // block, registers 8*(c%2)..+7 of tile c/2 (the PERM key order).
+    Frag<T> pf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[c][e] = (T)s[c >> 1][8 * (c & 1) + e];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mma16(acc[t], fr.col(vt, 16 * c, t), pf[c]);
+  };
+  for (int kb = 0; kb < nkb; kb += S) {
+    block(kb, std::integral_constant<int, 0>());
+    if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>());
+    if constexpr (S > 2) {
+      if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>());
     }
   }
 

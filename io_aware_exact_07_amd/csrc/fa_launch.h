@@ -27,7 +27,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;    // float32 [B,H,N] scratch: D_i = dO_i . o_i
+  float* lse2;     // float32 [B*H][Npad] scratch: lse_i * log2(e), +inf for rows >= L
+  float* delta;    // float32 [B*H][Npad] scratch: D_i = dO_i . o_i, 0 for rows >= L
   const int32_t* seqlens;
   int B, H, N;
   float scale;
@@ -37,6 +38,10 @@ struct BwdArgs {
 // The backward pass is three launches: stage 1 = D, stage 2 = dK and dV,
 // stage 3 = dQ.  Stages 2 and 3 each need only stage 1's D.
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
+
+// Rows per head of the backward's row vectors: N rounded up to a whole
+// number of 128-row blocks, so block-sized copies never run past a head.
+__host__ __device__ inline int padded_rows(int N) { return (N + 127) / 128 * 128; }
 hipError_t launch_bwd_stage(int stage, const BwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
 
 }  // namespace fa

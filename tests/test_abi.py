@@ -81,8 +81,9 @@ def test_backward_validation(kw, status):
 
 def test_stage_validation():
     ws = fa.fa_bwd_workspace_bytes(1, 1, 128, 64, fa.FA_BF16)
-    assert fa.fa_bwd_prepare(None, FAKE, 1, 1, 128, 64, None, FAKE, ws, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
-    assert fa.fa_bwd_prepare(FAKE, FAKE, 1, 1, 128, 64, None, FAKE, ws - 1, fa.FA_BF16, None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_prepare(None, FAKE, FAKE, 1, 1, 128, 64, None, FAKE, ws, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_prepare(FAKE, FAKE, None, 1, 1, 128, 64, None, FAKE, ws, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_prepare(FAKE, FAKE, FAKE, 1, 1, 128, 64, None, FAKE, ws - 1, fa.FA_BF16, None) == fa.FA_ERR_WORKSPACE
     assert fa.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 64, 0.1, 1, None, FAKE, ws,
                           fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 64, 0.1, 1, None, FAKE, ws,
@@ -95,12 +96,14 @@ def test_stage_validation():
                         None) == fa.FA_ERR_WORKSPACE
 
 
-def test_workspace_is_linear_in_N_and_holds_D():
+def test_workspace_is_linear_in_N_and_holds_row_vectors():
     for dt in (fa.FA_BF16, fa.FA_FP32):
         for d in (64, 128):
             ws = [fa.fa_bwd_workspace_bytes(2, 3, n, d, dt) for n in (512, 1024, 2048, 4096)]
             assert all(b == 2 * a for a, b in zip(ws, ws[1:]))
-            assert ws[0] == 2 * 3 * 512 * 4   # D only: one float32 per row
+            assert ws[0] == 2 * (2 * 3 * 512 * 4)   # D and lse2: one float32 each per row
+            # rows are padded to whole 128-row blocks per head
+            assert fa.fa_bwd_workspace_bytes(1, 1, 129, d, dt) == 2 * 256 * 4
     assert fa.fa_bwd_workspace_bytes(1, 1, 128, 96, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64, fa.FA_BF16) == 0
 

@@ -1,18 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of exact tiled attention (forward + recomputing backward) on one MI355X.
 
-One step = one forward and one backward pass (fa_fwd, then fa_bwd's three
+One step = one forward and one backward pass (fa_fwd, then fa_bwd's two
 stages) over the long-context GPT-2 head workload: B=1, H=12, N=8192, d=64,
 bf16, causal, Q and K scaled by 2 (inputs resident in HBM before timing).
 FLOPs are counted as 4*B*H*N^2*d forward and 2.5x that backward, halved for
 the causal mask.
 
 Prints one JSON line.  Besides the whole-step rate it carries:
-  roofline      the kernel with the longest average launch (of the forward,
-                the dK/dV stage and the dQ stage) against the bf16 dense
-                matrix-core peak: its algorithmic FLOPs (2*N^2*d per matrix
-                product per head, halved when causal, times the products the
-                kernel performs: 2 forward, 4 dK/dV, 3 dQ) over its average
+  roofline      the kernel with the longest average launch (the forward, or the
+                gradient kernel that runs the dK/dV and dQ blocks in one
+                launch) against the bf16 dense matrix-core peak: its
+                algorithmic FLOPs (2*N^2*d per matrix product per head, halved
+                when causal, times the products the kernel performs: 2
+                forward, 4 + 3 gradients) over its average
                 duration, timed with HIP events on the stream the kernels run
                 on; `traffic` is the HBM bytes per launch from rocprofv3
                 FETCH_SIZE + WRITE_SIZE counters recorded under profiles/ when
@@ -40,8 +41,7 @@ PEAK_HBM_GBS = 8000.0
 KERNELS = {
     # name: (source file, matrix products per score element)
     "fwd_kernel": ("io_aware_exact_07_amd/csrc/fa_fwd.hip", 2),
-    "bwd_dkdv_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 4),
-    "bwd_dq_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 3),
+    "bwd_grad_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 7),   # dK/dV (4) and dQ (3) blocks
 }
 
 
@@ -158,14 +158,10 @@ def main():
         st |= fa.fa_bwd_prepare(P[3], P[8], P[4], B, H, N, d, None, P[9], wsb, fa.FA_BF16, sp)
         if ev is not None:
             ev[1].record(stream)
-        st |= fa.fa_bwd_dkdv(P[0], P[1], P[2], P[8], P[4], P[6], P[7], B, H, N, d, scale, 1, None, P[9], wsb,
-                             fa.FA_BF16, sp)
+        st |= fa.fa_bwd_dkdv_dq(P[0], P[1], P[2], P[8], P[4], P[5], P[6], P[7], B, H, N, d, scale, 1, None, P[9],
+                                wsb, fa.FA_BF16, sp)
         if ev is not None:
             ev[2].record(stream)
-        st |= fa.fa_bwd_dq(P[0], P[1], P[2], P[8], P[4], P[5], B, H, N, d, scale, 1, None, P[9], wsb, fa.FA_BF16,
-                           sp)
-        if ev is not None:
-            ev[3].record(stream)
         if st != 0:
             raise RuntimeError(f"attention call failed: {st}")
 
@@ -175,7 +171,7 @@ def main():
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
     starts = [mk() for _ in range(K)]
-    marks = [[mk(), mk(), mk(), mk()] for _ in range(K)]
+    marks = [[mk(), mk(), mk()] for _ in range(K)]
     t_begin, t_end = mk(), mk()
     torch.cuda.synchronize()
     t_begin.record(stream)
@@ -189,20 +185,19 @@ def main():
     avg = lambda f: sum(f(i) for i in range(K)) / K
     fwd_ms = avg(lambda i: starts[i].elapsed_time(marks[i][0]))
     prep_ms = avg(lambda i: marks[i][0].elapsed_time(marks[i][1]))
-    dkdv_ms = avg(lambda i: marks[i][1].elapsed_time(marks[i][2]))
-    dq_ms = avg(lambda i: marks[i][2].elapsed_time(marks[i][3]))
-    bwd_ms = prep_ms + dkdv_ms + dq_ms
+    grads_ms = avg(lambda i: marks[i][1].elapsed_time(marks[i][2]))
+    bwd_ms = prep_ms + grads_ms
 
     f_fwd, f_bwd = w.flops()
     value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     per_product = f_fwd / 2.0
-    launches = {"fwd_kernel": fwd_ms, "bwd_dkdv_kernel": dkdv_ms, "bwd_dq_kernel": dq_ms}
+    launches = {"fwd_kernel": fwd_ms, "bwd_grad_kernel": grads_ms}
     dom = max(launches, key=launches.get)
     achieved = KERNELS[dom][1] * per_product / (launches[dom] * 1e-3) / 1e12
     e = 2
     compulsory = e * 4 * B * H * N * d + 4 * B * H * N                 # forward: q, k, v, o + lse
     compulsory += e * 2 * B * H * N * d + 4 * B * H * N                # prepare: o, dO -> D
-    compulsory += 2 * (e * 4 * B * H * N * d + 8 * B * H * N)          # dkdv, dq: q, k, v, dO, lse, D in
+    compulsory += e * 4 * B * H * N * d + 8 * B * H * N                # gradients: q, k, v, dO, lse2, D in
     compulsory += e * 3 * B * H * N * d                                # dk, dv, dq out
     rec = {
         "metric": METRIC,
@@ -221,7 +216,7 @@ def main():
                    "fwd_gflop": f_fwd / 1e9, "bwd_gflop": f_bwd / 1e9},
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
-        "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv": round(dkdv_ms, 5), "dq": round(dq_ms, 5)},
+        "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv_dq": round(grads_ms, 5)},
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -98,10 +98,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int dtype, void* stream);
 
 /*
- * The three launches fa_bwd makes, exposed for callers that time them
- * separately or run the two gradient stages concurrently.  Calling prepare,
- * then dkdv and dq (in either order, or on two streams ordered after
- * prepare) with one workspace is exactly fa_bwd.
+ * The stages of fa_bwd, exposed for callers that time them separately or
+ * schedule them themselves.  fa_bwd is prepare followed by dkdv_dq; prepare
+ * followed by dkdv and dq (in either order, or on two streams ordered after
+ * prepare) computes the same, bit for bit.
  *   prepare: D_i = dO_i . o_i and lse_i in base 2 into the workspace (reads
  *            o, dO, lse).  A row of the softmax-Jacobian product reduces to
  *            dS_ij = P_ij (dP_ij - D_i) because sum_j P_ij dP_ij = dO_i . o_i.
@@ -109,6 +109,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *            dk and dv (reads q, k, v, dO, lse and the prepared workspace).
  *   dq:      recomputes the score blocks query block by query block and
  *            writes dq (same inputs).
+ *   dkdv_dq: both of the above in one launch, their blocks interleaved
+ *            heaviest first (with a causal mask a lone list's heaviest blocks
+ *            outlast the average load of a resident workgroup).
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */
@@ -123,6 +126,10 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
               const float* lse, void* dq, int B, int H, int N, int d,
               float scale, int causal, const int32_t* seqlens, void* workspace,
               size_t workspace_bytes, int dtype, void* stream);
+int fa_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N,
+                   int d, float scale, int causal, const int32_t* seqlens, void* workspace,
+                   size_t workspace_bytes, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(int status);

@@ -6,7 +6,7 @@ PyTorch supplies device memory and the stream.  If the library has not been
 built the import of the native part fails loudly; there is no fallback.
 
 Raw entry points (same names and argument order as the C ABI, pointers as
-ints): fa_fwd, fa_bwd, fa_bwd_prepare, fa_bwd_dkdv, fa_bwd_dq,
+ints): fa_fwd, fa_bwd, fa_bwd_prepare, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dkdv_dq,
 fa_bwd_workspace_bytes, fa_status_string.
 Tensor helpers: forward(q, k, v, ...) -> (o, lse) and
 backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv).
@@ -58,6 +58,8 @@ def lib():
         L.fa_bwd_dkdv.restype = ci
         L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
         L.fa_bwd_dq.restype = ci
+        L.fa_bwd_dkdv_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
+        L.fa_bwd_dkdv_dq.restype = ci
         L.fa_status_string.argtypes = [ci]
         L.fa_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -90,6 +92,12 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, scale, causal, seqlens, workspac
               stream) -> int:
     return lib().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, scale, int(bool(causal)), seqlens, workspace,
                            workspace_bytes, dtype, stream)
+
+
+def fa_bwd_dkdv_dq(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, workspace, workspace_bytes,
+                   dtype, stream) -> int:
+    return lib().fa_bwd_dkdv_dq(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, scale, int(bool(causal)), seqlens,
+                                workspace, workspace_bytes, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:

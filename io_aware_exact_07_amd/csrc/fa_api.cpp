@@ -56,7 +56,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
 
 namespace {
 
-enum Stage { kAll = 0, kPrepare = 1, kDkDv = 2, kDq = 3 };
+enum Stage { kAll = 0, kPrepare = 1, kDkDv = 2, kDq = 3, kGrads = 4 };
 
 // Shared validation of the backward entry points; fills `a` on success.
 int bwd_setup(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -64,13 +64,14 @@ int bwd_setup(const void* q, const void* k, const void* v, const void* o, const 
               void* workspace, size_t workspace_bytes, int dtype, int stage, fa::BwdArgs* a) {
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
-  const bool compute = stage == kAll || stage == kDkDv || stage == kDq;
+  const bool compute = stage == kAll || stage == kDkDv || stage == kDq || stage == kGrads;
   if (compute && (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v))) return FA_ERR_INVALID_ARG;
   if ((stage == kAll || stage == kPrepare) && (!tensor_ok(o) || lse == nullptr || !aligned(lse, 4)))
     return FA_ERR_INVALID_ARG;
   if (!tensor_ok(dO)) return FA_ERR_INVALID_ARG;
-  if ((stage == kAll || stage == kDkDv) && (!tensor_ok(dk) || !tensor_ok(dv))) return FA_ERR_INVALID_ARG;
-  if ((stage == kAll || stage == kDq) && !tensor_ok(dq)) return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kDkDv || stage == kGrads) && (!tensor_ok(dk) || !tensor_ok(dv)))
+    return FA_ERR_INVALID_ARG;
+  if ((stage == kAll || stage == kDq || stage == kGrads) && !tensor_ok(dq)) return FA_ERR_INVALID_ARG;
   if (compute && (lse == nullptr || !aligned(lse, 4))) return FA_ERR_INVALID_ARG;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
@@ -81,13 +82,11 @@ int bwd_setup(const void* q, const void* k, const void* v, const void* o, const 
   return FA_OK;
 }
 
-int run_stages(int first, int last, const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
-  for (int s = first; s <= last; ++s) {
-    hipError_t e = fa::launch_bwd_stage(s, a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return FA_ERR_HIP;
-    }
+int run_stage(int stage, const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
+  hipError_t e = fa::launch_bwd_stage(stage, a, d, dtype, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
   }
   return FA_OK;
 }
@@ -102,7 +101,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                      kAll, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  return run_stages(kPrepare, kDq, a, d, dtype, causal, stream);
+  st = run_stage(kPrepare, a, d, dtype, causal, stream);
+  if (st != FA_OK) return st;
+  return run_stage(kGrads, a, d, dtype, causal, stream);
 }
 
 int fa_bwd_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -112,7 +113,7 @@ int fa_bwd_prepare(const void* o, const void* dO, const float* lse, int B, int H
                      workspace, workspace_bytes, dtype, kPrepare, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  return run_stages(kPrepare, kPrepare, a, d, dtype, 0, stream);
+  return run_stage(kPrepare, a, d, dtype, 0, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk, void* dv,
@@ -123,7 +124,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
                      workspace_bytes, dtype, kDkDv, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  return run_stages(kDkDv, kDkDv, a, d, dtype, causal, stream);
+  return run_stage(kDkDv, a, d, dtype, causal, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B, int H,
@@ -134,7 +135,18 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
                      workspace_bytes, dtype, kDq, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  return run_stages(kDq, kDq, a, d, dtype, causal, stream);
+  return run_stage(kDq, a, d, dtype, causal, stream);
+}
+
+int fa_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int N, int d, float scale, int causal, const int32_t* seqlens,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  fa::BwdArgs a;
+  int st = bwd_setup(q, k, v, nullptr, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, workspace, workspace_bytes,
+                     dtype, kGrads, &a);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  return run_stage(kGrads, a, d, dtype, causal, stream);
 }
 
 const char* fa_status_string(int status) {

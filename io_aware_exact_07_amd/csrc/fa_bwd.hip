@@ -85,46 +85,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // as column fragments in the matching order).  Query blocks are double
 // buffered: the next block's Q, dO, lse and D are fetched into registers
 // while the current one is computed, then parked in the idle buffer.
+template <typename T, int D>
+struct DkdvShape {
+  static constexpr int BK = 128;
+  static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // fp32 d=128 keeps its registers
+  static constexpr int S = 3;                                        // pipeline stages
+  static constexpr int TILE = BQ * D * (int)sizeof(T);               // bytes of one Q or dO tile
+  static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;                // Q, dO, lse2 | D
+  static constexpr int LDS = S * STAGE;
+};
+
+// One key block (BK keys of head bh): dK and dV.  `lds` holds S stages of
+// [Q tile | dO tile | lse2 | D].
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BK = 128, NT = kThreads;
-  constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // fp32 d=128 keeps its registers
+__device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const int bh, char* lds) {
+  using SH = DkdvShape<T, D>;
+  constexpr int BK = SH::BK, NT = kThreads;
+  constexpr int BQ = SH::BQ;
   constexpr int NC = D / 16;
   constexpr int NDT = D / 32;
   constexpr int NQT = BQ / 32;
-  // Three pipeline stages, each its own LDS arrays: Q and dO tiles (swizzled
-  // Tile<T, D>) and the block's lse2 | D row vectors, filled by direct
-  // HBM -> LDS copies issued two blocks ahead.
-  constexpr int S = 3;
-  __shared__ __attribute__((aligned(16))) T sQ0[BQ * D];
-  __shared__ __attribute__((aligned(16))) T sO0[BQ * D];
-  __shared__ __attribute__((aligned(16))) float sR0[2 * BQ];
-  __shared__ __attribute__((aligned(16))) T sQ1[BQ * D];
-  __shared__ __attribute__((aligned(16))) T sO1[BQ * D];
-  __shared__ __attribute__((aligned(16))) float sR1[2 * BQ];
-  __shared__ __attribute__((aligned(16))) T sQ2[BQ * D];
-  __shared__ __attribute__((aligned(16))) T sO2[BQ * D];
-  __shared__ __attribute__((aligned(16))) float sR2[2 * BQ];
-  auto qst = [&](auto STG) -> T* {
-    if constexpr (decltype(STG)::value == 0) return sQ0;
-    else if constexpr (decltype(STG)::value == 1) return sQ1;
-    else return sQ2;
-  };
-  auto ost = [&](auto STG) -> T* {
-    if constexpr (decltype(STG)::value == 0) return sO0;
-    else if constexpr (decltype(STG)::value == 1) return sO1;
-    else return sO2;
-  };
+  // Three pipeline stages: Q and dO tiles (swizzled Tile<T, D>) and the
+  // block's lse2 | D row vectors, filled by direct HBM -> LDS copies issued
+  // two blocks ahead.
+  constexpr int S = SH::S;
+  auto qst = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE); };
+  auto ost = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE + SH::TILE); };
   auto rst = [&](auto STG) -> float* {
-    if constexpr (decltype(STG)::value == 0) return sR0;
-    else if constexpr (decltype(STG)::value == 1) return sR1;
-    else return sR2;
+    return reinterpret_cast<float*>(lds + decltype(STG)::value * SH::STAGE + 2 * SH::TILE);
   };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
-  const int BH = a.B * a.H;
-  const int kb = blockIdx.x / BH;  // causal: low key blocks see the most queries and go first
-  const int bh = blockIdx.x % BH;
   const int b = bh / a.H;
   const int L = clamp_len(a.seqlens, b, a.N);
   const size_t hoff = (size_t)bh * a.N * D;
@@ -292,37 +283,34 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
 // dP^T = V dO^T (a lane owns one query, so lse_i and D_i are per-lane
 // scalars), forms dS^T in registers and accumulates dQ^T += K^T dS^T with
 // dS^T as the contraction operand straight from registers.
+template <typename T, int D>
+struct DqShape {
+  static constexpr int BQ = 128, BK = 64;
+  static constexpr int S = (sizeof(T) == 2 && D == 64) ? 3 : 2;  // pipeline stages
+  static constexpr int TILE = BK * D * (int)sizeof(T);            // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LDS = S * STAGE;
+};
+
+// One query block (BQ queries of head bh): dQ.  `lds` holds S stages of
+// [K tile | V tile].
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BQ = 128, BK = 64, NT = kThreads;
+__device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const int bh, char* lds) {
+  using SH = DqShape<T, D>;
+  constexpr int BQ = SH::BQ, BK = SH::BK, NT = kThreads;
   constexpr int NC = D / 16;
   constexpr int NDT = D / 32;
   // Pipeline stages as in the forward kernel: K/V blocks copied HBM -> LDS
-  // S-1 blocks ahead, each stage its own LDS arrays.
-  constexpr int S = (sizeof(T) == 2 && D == 64) ? 3 : 2;
-  constexpr int TS = BK * D, TS2 = S > 2 ? BK * D : 8;
-  __shared__ __attribute__((aligned(16))) T sK0[TS];  // swizzled Tile<T, D>
-  __shared__ __attribute__((aligned(16))) T sV0[TS];
-  __shared__ __attribute__((aligned(16))) T sK1[TS];
-  __shared__ __attribute__((aligned(16))) T sV1[TS];
-  __shared__ __attribute__((aligned(16))) T sK2[TS2];
-  __shared__ __attribute__((aligned(16))) T sV2[TS2];
-  auto kst = [&](auto STG) -> T* {
-    if constexpr (decltype(STG)::value == 0) return sK0;
-    else if constexpr (decltype(STG)::value == 1) return sK1;
-    else return sK2;
-  };
-  auto vst = [&](auto STG) -> T* {
-    if constexpr (decltype(STG)::value == 0) return sV0;
-    else if constexpr (decltype(STG)::value == 1) return sV1;
-    else return sV2;
-  };
+  // S-1 blocks ahead.
+  constexpr int S = SH::S;
+  auto kst = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE); };
+  auto vst = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE + SH::TILE); };
+  T* sK0 = kst(std::integral_constant<int, 0>());
+  T* sV0 = vst(std::integral_constant<int, 0>());
+  T* sK1 = kst(std::integral_constant<int, 1>());
+  T* sV1 = vst(std::integral_constant<int, 1>());
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
-  const int BH = a.B * a.H;
-  const int nqb = (a.N + BQ - 1) / BQ;
-  const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
   const int b = bh / a.H;
   const int L = clamp_len(a.seqlens, b, a.N);
   const size_t hoff = (size_t)bh * a.N * D;
@@ -438,6 +426,35 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gradient kernel.  MODE 1: dK/dV blocks only; MODE 2: dQ blocks only;
+// MODE 0: both job lists in one launch.  With a causal mask the work of a
+// block ranges from one block-step to N/64, and a lone launch of either list
+// has its heaviest blocks longer than the average per resident workgroup.
+// Interleaving the two independent lists heaviest-first (rank r of each list
+// in turn, every head) doubles the work per slot so the greedy dispatch
+// balances it.  Both bodies share one LDS allocation.
+template <typename T, int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_grad_kernel(BwdArgs a) {
+  constexpr int LDS = DkdvShape<T, D>::LDS > DqShape<T, D>::LDS ? DkdvShape<T, D>::LDS : DqShape<T, D>::LDS;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  const int BH = a.B * a.H;
+  const int nb = (a.N + 127) / 128;  // 128-row blocks: key blocks of dK/dV, query blocks of dQ
+  int i = blockIdx.x;
+  bool dkdv = MODE == 1;
+  if (MODE == 0) {
+    const int r = i / (2 * BH), j = i % (2 * BH);
+    dkdv = j < BH;
+    i = r * BH + (dkdv ? j : j - BH);
+  }
+  const int rank = i / BH, bh = i % BH;
+  if (dkdv) {
+    if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL>(a, rank, bh, lds);  // causal: low key blocks are heaviest
+  } else {
+    if constexpr (MODE != 1) dq_block<T, D, CAUSAL>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
+  }
+}
+
 unsigned grid_for(long long work, int threads) {
   long long g = (work + threads - 1) / threads;
   if (g > 65536LL * 8) g = 65536LL * 8;
@@ -452,11 +469,13 @@ hipError_t launch_one(int stage, const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid_for(rows * CPR, 256)), dim3(256), 0, stream, a);
   } else {
     const long long grid = (long long)((a.N + 127) / 128) * a.B * a.H;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (2 * grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (stage == 2)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    else if (stage == 3)
+      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 0>), dim3((unsigned)(2 * grid)), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

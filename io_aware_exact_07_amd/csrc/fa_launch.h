@@ -35,8 +35,8 @@ struct BwdArgs {
 };
 
 // Return hipSuccess or the launch error.  dtype: 0 = bf16, 1 = fp32.
-// The backward pass is three launches: stage 1 = D, stage 2 = dK and dV,
-// stage 3 = dQ.  Stages 2 and 3 each need only stage 1's D.
+// Backward stages: 1 = the row vectors (D, lse in base 2), 2 = dK and dV,
+// 3 = dQ, 4 = dK, dV and dQ in one launch.  Stages 2-4 need only stage 1.
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool causal, hipStream_t stream);
 
 // Rows per head of the backward's row vectors: N rounded up to a whole

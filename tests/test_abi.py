@@ -94,6 +94,10 @@ def test_stage_validation():
                         None) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.1, 1, None, None, ws, fa.FA_BF16,
                         None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_dkdv_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 64, 0.1, 1, None, FAKE, ws,
+                             fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_dkdv_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.1, 1, None, FAKE, 8,
+                             fa.FA_BF16, None) == fa.FA_ERR_WORKSPACE
 
 
 def test_workspace_is_linear_in_N_and_holds_row_vectors():

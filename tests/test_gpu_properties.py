@@ -109,3 +109,29 @@ def test_workspace_and_memory_are_linear_in_N():
     n = sizes[-1]
     expected = 4 * (12 * n * 64 * 2) + 12 * n * 4 + ws[-1]   # o, dq, dk, dv + lse + workspace
     assert peaks[-1] <= 1.05 * expected, (peaks[-1], expected)
+
+
+def test_separate_and_fused_gradient_stages_agree_bitwise():
+    """fa_bwd (prepare + one fused dK/dV/dQ launch) equals prepare + dkdv + dq."""
+    for causal, seqlens in ((True, None), (False, [300, 77])):
+        inp = W.random_inputs(2, 3, 300, 64, "bf16", seed=21, gain=1.5, seqlens=seqlens)
+        q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+        sl = None if inp["seqlens"] is None else inp["seqlens"].to(DEV)
+        o, lse = fa.forward(q, k, v, causal=causal, seqlens=sl)
+        ref = fa.backward(q, k, v, o, do, lse, causal=causal, seqlens=sl)
+        B, H, N, d = q.shape
+        wsb = fa.fa_bwd_workspace_bytes(B, H, N, d, fa.FA_BF16)
+        ws = torch.empty(wsb, device=DEV, dtype=torch.uint8)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        sp = torch.cuda.current_stream().cuda_stream
+        slp = None if sl is None else sl.data_ptr()
+        assert fa.fa_bwd_prepare(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, N, d, slp, ws.data_ptr(), wsb,
+                                 fa.FA_BF16, sp) == 0
+        assert fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                            B, H, N, d, 0.125, causal, slp, ws.data_ptr(), wsb, fa.FA_BF16, sp) == 0
+        assert fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), B, H, N, d, 0.125, causal, slp, ws.data_ptr(), wsb,
+                              fa.FA_BF16, sp) == 0
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (dq, dk, dv)):
+            assert torch.equal(a, b)

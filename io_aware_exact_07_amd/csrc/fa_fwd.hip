@@ -34,6 +34,7 @@ constexpr int kFwdBQ = 128;
 constexpr int kFwdBK = 64;
 constexpr int kFwdThreads = 256;
 constexpr float kSlack = 8.0f;  // probabilities are formed relative to a max at most 2^8 stale
+constexpr int kCUs = 256;        // compute units of an MI355X: the dispatch stride that shares a CU
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
@@ -66,9 +67,18 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
   const int nqb = (a.N + BQ - 1) / BQ;
-  // Causal: heaviest query blocks (most keys) are dispatched first.
-  const int qb = CAUSAL ? (nqb - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  // Causal: block work grows with the query block index.  Workgroups are
+  // dispatched in index order across the CUs, so indices i, i + kCUs,
+  // i + 2 kCUs, ... tend to share a CU.  Ranking blocks heaviest first and
+  // reversing every other group of kCUs pairs heavy with light blocks on a CU.
+  int idx = blockIdx.x;
+  if (CAUSAL) {
+    const int g = idx / kCUs, t = idx % kCUs;
+    const int total = (int)gridDim.x;
+    if ((g & 1) && (g + 1) * kCUs <= total) idx = g * kCUs + (kCUs - 1 - t);
+  }
+  const int qb = CAUSAL ? (nqb - 1 - idx / BH) : idx / BH;
+  const int bh = idx % BH;
   const int b = bh / a.H;
   const int L = clamp_len(a.seqlens, b, a.N);
   const size_t hoff = (size_t)bh * a.N * D;

@@ -21,7 +21,11 @@ Prints one JSON line.  Besides the whole-step rate it carries:
   cpu_baseline  the fp64 CPU oracle timed on this host on whole heads of the
                 same workload (about 10 s of work), in the same unit
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --copy-probe   (plain 256 MiB copy, for counter calibration)
+       python bench.py --copy-probe        (plain 256 MiB copy, for counter calibration)
+       python bench.py --memory-scaling    (JSON lines: peak memory of a 12-layer GPT-2-config
+                                            causal attention stack, N = 512..32768, vs the
+                                            recomputation page's model and explicit attention)
+       python bench.py --compare-explicit  (JSON lines: fwd+bwd time vs explicit attention)
 """
 from __future__ import annotations
 
@@ -88,6 +92,123 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}), flush=True)
 
 
+def explicit_attention_step(q, k, v, do, scale, causal):
+    """Standard attention that materialises the score and probability
+    matrices (the baseline the recomputation pages compare against), forward
+    and backward by hand in the input dtype.  Every batched product gets
+    contiguous operands.  Used only to measure memory and time beside the
+    tiled path; returns (o, dq, dk, dv)."""
+    import torch
+    N = q.shape[2]
+    kt = k.transpose(-1, -2).contiguous()
+    s = torch.matmul(q, kt).float() * scale
+    if causal:
+        s.masked_fill_(torch.ones(N, N, dtype=torch.bool, device=q.device).triu_(1), float("-inf"))
+    p = torch.softmax(s, dim=-1).to(q.dtype)
+    del s
+    o = torch.matmul(p, v)
+    pt = p.transpose(-1, -2).contiguous()
+    dv = torch.matmul(pt, do)
+    del pt
+    vt = v.transpose(-1, -2).contiguous()
+    dp = torch.matmul(do, vt).float()
+    pf = p.float()
+    ds = (pf * (dp - (pf * dp).sum(-1, keepdim=True))).to(q.dtype)
+    del dp, pf
+    dq = torch.matmul(ds, k) * scale
+    dst = ds.transpose(-1, -2).contiguous()
+    dk = torch.matmul(dst, q) * scale
+    return o, dq, dk, dv
+
+
+def memory_scaling(seq_lens=(512, 2048, 8192, 32768), layers=12, d_model=768, heads=12):
+    """Peak device memory of a stack of causal attention layers (GPT-2 config),
+    forward and backward through the autograd binding, against the recomputation
+    page's training-memory model and (where it fits) explicit attention."""
+    import torch
+    from io_aware_exact_07_amd.autograd import attention
+    from oracle.memory_model import training_memory
+    dev = torch.device("cuda:0")
+    d = d_model // heads
+    for N in seq_lens:
+        g = torch.Generator("cpu").manual_seed(N)
+        qkv = [[torch.randn(1, heads, N, d, generator=g).to(dev, torch.bfloat16).requires_grad_() for _ in range(3)]
+               for _ in range(layers)]
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        outs = [attention(q, k, v, causal=True) for q, k, v in qkv]
+        torch.cuda.synchronize()
+        stored = torch.cuda.memory_allocated() - base
+        loss = sum(o.float().square().sum() for o in outs)
+        loss.backward()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        inputs = sum(t.numel() * t.element_size() for l in qkv for t in l)
+        model = training_memory(N, d_model=d_model, heads=heads, layers=layers, elem_bytes=2)
+        rec = {"mode": "memory_scaling", "N": N, "layers": layers, "d_model": d_model, "heads": heads,
+               "inputs_qkv_bytes": inputs, "stored_after_forward_bytes": stored,
+               "stored_incl_qkv_bytes": stored + inputs,
+               "model_recompute_bytes": round(model.recompute_gb * 1e9),
+               "model_standard_bytes": round(model.standard_gb * 1e9),
+               "peak_fwd_bwd_extra_bytes": peak}
+        del outs, loss, qkv
+        torch.cuda.empty_cache()
+        # explicit attention for one layer, where its N x N matrices fit comfortably
+        if model.attn_matrix_gb / layers < 40:
+            q, k, v, do = (torch.randn(1, heads, N, d, generator=g).to(dev, torch.bfloat16) for _ in range(4))
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            b0 = torch.cuda.memory_allocated()
+            r = explicit_attention_step(q, k, v, do, 1.0 / d ** 0.5, True)
+            torch.cuda.synchronize()
+            rec["explicit_one_layer_peak_extra_bytes"] = torch.cuda.max_memory_allocated() - b0
+            del r, q, k, v, do
+            torch.cuda.empty_cache()
+        else:
+            rec["explicit_one_layer_peak_extra_bytes"] = None
+        print(json.dumps(rec), flush=True)
+
+
+def compare_explicit(steps=10):
+    """fwd+bwd time of the tiled path vs explicit attention on the same inputs."""
+    import torch
+    import io_aware_exact_07_amd as fa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    for w in (W.GPT2_SMALL, W.BERT_LARGE_PADDED, W.GPT2_LONG):
+        inp = W.make_inputs(w)
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        sl = None if inp["seqlens"] is None else inp["seqlens"].to(dev)
+
+        def ours():
+            o, lse = fa.forward(q, k, v, causal=w.causal, seqlens=sl)
+            fa.backward(q, k, v, o, do, lse, causal=w.causal, seqlens=sl)
+
+        def explicit():
+            explicit_attention_step(q, k, v, do, w.softmax_scale, w.causal)
+
+        res = {"mode": "compare_explicit", "workload": w.name}
+        for name, fn in (("tiled", ours), ("explicit", explicit if sl is None else None)):
+            if fn is None:
+                res[name + "_ms"] = None   # explicit baseline has no key-padding mask
+                continue
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            res[name + "_ms"] = round(a.elapsed_time(b) / steps, 4)
+        if res.get("explicit_ms"):
+            res["speedup"] = round(res["explicit_ms"] / res["tiled_ms"], 2)
+        print(json.dumps(res), flush=True)
+        del q, k, v, do
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, min_seconds=10.0):
     """The oracle as it stands, on whole heads of the workload (as many as fit
     in about min_seconds, at least one), on this host's cores."""
@@ -122,6 +243,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--memory-scaling", action="store_true",
+                    help="peak memory of a 12-layer causal attention stack vs the page's model")
+    ap.add_argument("--compare-explicit", action="store_true",
+                    help="time the tiled path against explicit attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -130,6 +255,12 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.memory_scaling:
+        memory_scaling()
+        return
+    if args.compare_explicit:
+        compare_explicit()
         return
 
     import torch

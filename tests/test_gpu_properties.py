@@ -135,3 +135,45 @@ def test_separate_and_fused_gradient_stages_agree_bitwise():
         torch.cuda.synchronize()
         for a, b in zip(ref, (dq, dk, dv)):
             assert torch.equal(a, b)
+
+
+def test_autograd_binding_matches_direct_calls_and_oracle():
+    from io_aware_exact_07_amd.autograd import attention
+    import oracle
+    inp = W.random_inputs(1, 2, 150, 64, "bf16", seed=33, gain=1.5)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    qr, kr, vr = (t.clone().requires_grad_() for t in (q, k, v))
+    o = attention(qr, kr, vr, causal=True)
+    o.backward(do)
+    o2, lse = fa.forward(q, k, v, causal=True)
+    g = fa.backward(q, k, v, o2, do, lse, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for a, b in zip((qr.grad, kr.grad, vr.grad), g):
+        assert torch.equal(a, b)
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], 0.125, causal=True)
+    import numpy as np
+    err = np.max(np.abs(qr.grad.float().cpu().numpy() - ref["dq"])) / np.max(np.abs(ref["dq"]))
+    assert err < 5e-2
+
+
+def test_stored_activations_equal_the_recomputation_page_model():
+    """A 12-layer GPT-2-config causal stack through the autograd binding keeps
+    exactly what the page's training-memory model counts for the recomputing
+    method: Q, K, V, O per layer plus two 16-bit row statistics per (position,
+    head) -- here one float32 lse (Brenndoerfer, code cell In[17] / Out[18])."""
+    from io_aware_exact_07_amd.autograd import attention
+    from oracle.memory_model import training_memory
+    for N in (512, 2048):
+        g = torch.Generator("cpu").manual_seed(N)
+        qkv = [[torch.randn(1, 12, N, 64, generator=g).to(DEV, torch.bfloat16).requires_grad_() for _ in range(3)]
+               for _ in range(12)]
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        outs = [attention(q, k, v, causal=True) for q, k, v in qkv]
+        torch.cuda.synchronize()
+        stored = torch.cuda.memory_allocated() - base
+        inputs = sum(t.numel() * t.element_size() for l in qkv for t in l)
+        model = training_memory(N, d_model=768, heads=12, layers=12, elem_bytes=2)
+        assert stored + inputs == round(model.recompute_gb * 1e9)
+        del outs, qkv

@@ -58,7 +58,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scale or dtype */
-  FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64, 96 or 128 */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_HIP = -4          /* a kernel launch failed */
 } fa_status;
@@ -67,7 +67,8 @@ typedef enum {
  * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32).
  * The score matrix exists only tile by tile in registers; no N x N buffer is
  * ever formed (SOTA-087, "Why recomputation is cheaper here than storing").
- * scale must be finite and > 0.  d must be 64 or 128.
+ * scale must be finite and > 0.  d must be 64, 96 or 128 (the head
+ * dimensions of 64-128 the pages discuss, in 32-wide matrix-core tiles).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,

@@ -19,7 +19,7 @@ int check_common(int B, int H, int N, int d, float scale, int dtype) {
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_INVALID_ARG;
   if (B < 0 || H < 0 || N < 0 || N > kMaxN) return FA_ERR_INVALID_ARG;
   if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || N == 0) return 1;
   return FA_OK;
@@ -153,7 +153,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64, 96 or 128)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";

@@ -42,7 +42,8 @@ constexpr int kThreads = 256;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int EPC = 16 / sizeof(T);
-  constexpr int CPR = D / EPC;  // 16-byte chunks per row: 8, 16 or 32
+  constexpr int CHUNKS = D / EPC;  // 16-byte chunks per row: 8, 12, 16, 24 or 32
+  constexpr int CPR = CHUNKS <= 8 ? 8 : CHUNKS <= 16 ? 16 : 32;  // lanes per row (power of two)
   const int Np = padded_rows(a.N);
   const long long rows = (long long)a.B * a.H * Np;
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int L = prow < rows ? clamp_len(a.seqlens, (int)(bh / a.H), a.N) : 0;
     const bool in = prow < rows && pos < L;
     float dot = 0.f;
-    if (in) {
+    if (in && part < CHUNKS) {
       const long long row = bh * a.N + pos;
       const uint4 ov = *reinterpret_cast<const uint4*>(O + row * D + part * EPC);
       const uint4 dv = *reinterpret_cast<const uint4*>(dO + row * D + part * EPC);
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 template <typename T, int D>
 struct DkdvShape {
   static constexpr int BK = 128;
-  static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // fp32 d=128 keeps its registers
+  static constexpr int BQ = (sizeof(T) == 4 && D > 64) ? 32 : 64;  // fp32 d=96, 128 keep their registers
   static constexpr int S = 3;                                        // pipeline stages
   static constexpr int TILE = BQ * D * (int)sizeof(T);               // bytes of one Q or dO tile
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;                // Q, dO, lse2 | D
@@ -463,7 +464,8 @@ unsigned grid_for(long long work, int threads) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_one(int stage, const BwdArgs& a, hipStream_t stream) {
-  constexpr int CPR = D * (int)sizeof(T) / 16;
+  constexpr int CHUNKS = D * (int)sizeof(T) / 16;
+  constexpr int CPR = CHUNKS <= 8 ? 8 : CHUNKS <= 16 ? 16 : 32;
   const long long rows = (long long)a.B * a.H * padded_rows(a.N);
   if (stage == 1) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid_for(rows * CPR, 256)), dim3(256), 0, stream, a);
@@ -488,9 +490,14 @@ hipError_t launch_mask(int stage, const BwdArgs& a, bool causal, hipStream_t str
 }  // namespace
 
 hipError_t launch_bwd_stage(int stage, const BwdArgs& a, int d, int dtype, bool causal, hipStream_t stream) {
-  if (dtype == 0)
-    return d == 64 ? launch_mask<bf16, 64>(stage, a, causal, stream) : launch_mask<bf16, 128>(stage, a, causal, stream);
-  return d == 64 ? launch_mask<float, 64>(stage, a, causal, stream) : launch_mask<float, 128>(stage, a, causal, stream);
+  if (dtype == 0) {
+    if (d == 64) return launch_mask<bf16, 64>(stage, a, causal, stream);
+    if (d == 96) return launch_mask<bf16, 96>(stage, a, causal, stream);
+    return launch_mask<bf16, 128>(stage, a, causal, stream);
+  }
+  if (d == 64) return launch_mask<float, 64>(stage, a, causal, stream);
+  if (d == 96) return launch_mask<float, 96>(stage, a, causal, stream);
+  return launch_mask<float, 128>(stage, a, causal, stream);
 }
 
 }  // namespace fa

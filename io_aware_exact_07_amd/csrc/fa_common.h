@@ -81,21 +81,36 @@ template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
 //       (row fragments, ds_read_b128);
 //   (b) 32 lanes read 4 consecutive chunks of 4 consecutive rows, rows and
 //       chunks aligned to 4 (column fragments, ds_read_b64_tr_b16).
-// With 128-byte rows (8 chunks) the row's swizzle f takes bits 1..3 of the
-// row so that rows 2 apart differ in bit 2; with >= 256-byte rows it makes
-// the 4 rows of (b) differ in bits 2..3.  Each f is a permutation over 16
-// consecutive rows, which (a) needs.
+// With 128-byte rows (8 chunks) the row's XOR key takes bits 1..3 of the
+// row so that rows 2 apart differ in bit 2; with 256- or 512-byte rows it
+// makes the 4 rows of (b) differ in bits 2..3.  Each key is a permutation
+// over 16 consecutive rows, which (a) needs.  Rows of 12 or 24 chunks (head
+// dimension 96) rotate the chunks by (row/4) % 4 instead: consecutive rows
+// then start 12 or 24 chunks apart, so rows r and r+1 already fall 4 or 8
+// chunk slots apart and the rotation separates the four 4-row groups.  Every
+// key repeats every 16 rows, so adding whole 16-row blocks to a fragment's
+// row never changes its column placement.
 template <typename T, int D>
 struct Tile {
   static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;         // chunks per row
-  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "unsupported row length");
+  static constexpr bool ROT = CPR % 12 == 0;
+  static_assert(CPR == 8 || CPR == 12 || CPR == 16 || CPR == 24 || CPR == 32, "unsupported row length");
   __device__ __forceinline__ static int swz(int row) {
     return CPR == 8 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
   }
+  // Physical chunk of logical chunk j in `row`, and the inverse.
+  __device__ __forceinline__ static int phys(int row, int j) {
+    if constexpr (ROT) return (j + ((row >> 2) & 3)) % CPR;
+    else return j ^ swz(row);
+  }
+  __device__ __forceinline__ static int logical(int row, int pc) {
+    if constexpr (ROT) return (pc + CPR - ((row >> 2) & 3)) % CPR;
+    else return pc ^ swz(row);
+  }
   // Element offset of (row, col); col % EPC is preserved.
   __device__ __forceinline__ static int off(int row, int col) {
-    return row * D + ((((col / EPC) ^ swz(row)) * EPC) | (col % EPC));
+    return row * D + phys(row, col / EPC) * EPC + (col % EPC);
   }
 };
 
@@ -315,7 +330,7 @@ struct TileDma {
       const int P = (u * NW + w) * 64 + lane;
       const int row = P / CPR, pc = P % CPR;
       prow[u] = row;
-      gofs[u] = row * D + (pc ^ Tile<T, D>::swz(row)) * EPC;
+      gofs[u] = row * D + Tile<T, D>::logical(row, pc) * EPC;
     }
   }
   __device__ __forceinline__ void issue(const T* g, int r0, int nrows, T* lds, int tid) const {

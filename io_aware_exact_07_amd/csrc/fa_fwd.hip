@@ -236,9 +236,11 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, int d, int dtype, bool causal, hipStream_t stream) {
   if (dtype == 0) {
     if (d == 64) return causal ? launch_one<bf16, 64, true>(a, stream) : launch_one<bf16, 64, false>(a, stream);
+    if (d == 96) return causal ? launch_one<bf16, 96, true>(a, stream) : launch_one<bf16, 96, false>(a, stream);
     return causal ? launch_one<bf16, 128, true>(a, stream) : launch_one<bf16, 128, false>(a, stream);
   }
   if (d == 64) return causal ? launch_one<float, 64, true>(a, stream) : launch_one<float, 64, false>(a, stream);
+  if (d == 96) return causal ? launch_one<float, 96, true>(a, stream) : launch_one<float, 96, false>(a, stream);
   return causal ? launch_one<float, 128, true>(a, stream) : launch_one<float, 128, false>(a, stream);
 }
 

@@ -49,7 +49,7 @@ def bwd(**kw):
     (dict(lse=None), fa.FA_ERR_INVALID_ARG),
     (dict(o=FAKE + 2), fa.FA_ERR_INVALID_ARG),          # misaligned
     (dict(seqlens=FAKE + 2), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
@@ -102,13 +102,13 @@ def test_stage_validation():
 
 def test_workspace_is_linear_in_N_and_holds_row_vectors():
     for dt in (fa.FA_BF16, fa.FA_FP32):
-        for d in (64, 128):
+        for d in (64, 96, 128):
             ws = [fa.fa_bwd_workspace_bytes(2, 3, n, d, dt) for n in (512, 1024, 2048, 4096)]
             assert all(b == 2 * a for a, b in zip(ws, ws[1:]))
             assert ws[0] == 2 * (2 * 3 * 512 * 4)   # D and lse2: one float32 each per row
             # rows are padded to whole 128-row blocks per head
             assert fa.fa_bwd_workspace_bytes(1, 1, 129, d, dt) == 2 * 256 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 1, 128, 96, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 128, 80, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64, fa.FA_BF16) == 0
 
 

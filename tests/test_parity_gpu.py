@@ -58,6 +58,10 @@ SMALL = [
     (2, 1, 190, 64, "fp32", True, None),
     (2, 1, 160, 128, "fp32", False, [99, 160]),
     (1, 1, 333, 128, "fp32", True, None),
+    # head dimension 96 (the pages' d = 64..128 range in 32-wide tiles)
+    (2, 2, 300, 96, "bf16", True, None),
+    (2, 1, 257, 96, "bf16", False, [257, 130]),
+    (1, 1, 200, 96, "fp32", True, None),
 ]
 
 

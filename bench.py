@@ -21,6 +21,10 @@ Prints one JSON line.  Besides the whole-step rate it carries:
   cpu_baseline  the fp64 CPU oracle timed on this host on whole heads of the
                 same workload (about 10 s of work), in the same unit
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload gpt2_long|gpt2_small|bert_large|very_long|single_head]
+                       [--head-dim 64|96|128]
+       (the same JSON line for another workload; `traffic` is reported only
+        for the default one, whose counters are recorded)
        python bench.py --copy-probe        (plain 256 MiB copy, for counter calibration)
        python bench.py --memory-scaling    (JSON lines: peak memory of a 12-layer GPT-2-config
                                             causal attention stack, N = 512..32768, vs the
@@ -30,6 +34,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -41,7 +46,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd TFLOP/s at 1 MI355X (bf16, d=64, N=1k–32k); % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix-core peak
+PEAK_FP32_TFLOPS = 157.3   # MI355X published dense fp32 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+# --workload choices -> workloads module attribute
+WORKLOAD_KEYS = {"single_head": "SINGLE_HEAD_FP32", "gpt2_small": "GPT2_SMALL", "bert_large": "BERT_LARGE_PADDED",
+                 "gpt2_long": "GPT2_LONG", "very_long": "VERY_LONG"}
 KERNELS = {
     # name: (source file, matrix products per score element)
     "fwd_kernel": ("io_aware_exact_07_amd/csrc/fa_fwd.hip", 2),
@@ -247,6 +256,10 @@ def main():
                     help="peak memory of a 12-layer causal attention stack vs the page's model")
     ap.add_argument("--compare-explicit", action="store_true",
                     help="time the tiled path against explicit attention")
+    ap.add_argument("--workload", default="gpt2_long", choices=sorted(WORKLOAD_KEYS),
+                    help="which synthetic workload a step runs (default: the long-context GPT-2 head)")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="override the workload's head dimension (64, 96 or 128)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -267,15 +280,22 @@ def main():
     import io_aware_exact_07_amd as fa
     import workloads as W
 
-    w = W.GPT2_LONG
+    w = getattr(W, WORKLOAD_KEYS[args.workload])
+    if args.head_dim is not None and args.head_dim != w.d:
+        w = dataclasses.replace(w, d=args.head_dim, name=f"{w.name} (head dimension {args.head_dim})", scale=None)
+    default_workload = args.workload == "gpt2_long" and w.d == W.GPT2_LONG.d
     dev = torch.device("cuda:0")
     inp = W.make_inputs(w)
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    sl = None if inp["seqlens"] is None else inp["seqlens"].to(dev)
+    slp = None if sl is None else sl.data_ptr()
     B, H, N, d = q.shape
+    dt = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
+    causal = 1 if w.causal else 0
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    wsb = fa.fa_bwd_workspace_bytes(B, H, N, d, fa.FA_BF16)
+    wsb = fa.fa_bwd_workspace_bytes(B, H, N, d, dt)
     ws = torch.empty(wsb, device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -283,14 +303,14 @@ def main():
     P = [t.data_ptr() for t in (q, k, v, o, lse, dq, dk, dv, do, ws)]
 
     def step(ev=None):
-        st = fa.fa_fwd(P[0], P[1], P[2], P[3], P[4], B, H, N, d, scale, 1, None, fa.FA_BF16, sp)
+        st = fa.fa_fwd(P[0], P[1], P[2], P[3], P[4], B, H, N, d, scale, causal, slp, dt, sp)
         if ev is not None:
             ev[0].record(stream)
-        st |= fa.fa_bwd_prepare(P[3], P[8], P[4], B, H, N, d, None, P[9], wsb, fa.FA_BF16, sp)
+        st |= fa.fa_bwd_prepare(P[3], P[8], P[4], B, H, N, d, slp, P[9], wsb, dt, sp)
         if ev is not None:
             ev[1].record(stream)
-        st |= fa.fa_bwd_dkdv_dq(P[0], P[1], P[2], P[8], P[4], P[5], P[6], P[7], B, H, N, d, scale, 1, None, P[9],
-                                wsb, fa.FA_BF16, sp)
+        st |= fa.fa_bwd_dkdv_dq(P[0], P[1], P[2], P[8], P[4], P[5], P[6], P[7], B, H, N, d, scale, causal, slp,
+                                P[9], wsb, dt, sp)
         if ev is not None:
             ev[2].record(stream)
         if st != 0:
@@ -325,11 +345,12 @@ def main():
     launches = {"fwd_kernel": fwd_ms, "bwd_grad_kernel": grads_ms}
     dom = max(launches, key=launches.get)
     achieved = KERNELS[dom][1] * per_product / (launches[dom] * 1e-3) / 1e12
-    e = 2
+    e = 2 if w.dtype == "bf16" else 4
     compulsory = e * 4 * B * H * N * d + 4 * B * H * N                 # forward: q, k, v, o + lse
     compulsory += e * 2 * B * H * N * d + 4 * B * H * N                # prepare: o, dO -> D
     compulsory += e * 4 * B * H * N * d + 8 * B * H * N                # gradients: q, k, v, dO, lse2, D in
     compulsory += e * 3 * B * H * N * d                                # dk, dv, dq out
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -341,25 +362,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": True,
-                   "fwd_gflop": f_fwd / 1e9, "bwd_gflop": f_bwd / 1e9},
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "key_padding": sl is not None, "fwd_gflop": f_fwd / 1e9, "bwd_gflop": f_bwd / 1e9},
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
         "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv_dq": round(grads_ms, 5)},
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
-        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_peak": round(100.0 * value / peak, 2),
         "compulsory_hbm_gbs": round(compulsory / (ms * 1e-3) / 1e9, 1),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
             "achieved": round(achieved, 3),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_traffic(dom),
+            "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(dom) if default_workload else None,
             "avg_launch_ms": round(launches[dom], 5),
         },
     }

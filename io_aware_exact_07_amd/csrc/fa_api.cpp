@@ -91,6 +91,23 @@ int run_stage(int stage, const fa::BwdArgs& a, int d, int dtype, int causal, voi
   return FA_OK;
 }
 
+// Both gradient stages.  Under a causal mask or per-sequence lengths the
+// blocks of a lone dK/dV or dQ launch differ in work, and its heaviest blocks
+// run on after the rest of the grid has drained; one launch that interleaves
+// the two lists heaviest first evens the load out.  With equal blocks there
+// is nothing to even out, and when the operands the two lists stream (Q, dO
+// and K, V of every head) no longer fit the 256 MB last-level cache
+// together, running the lists one after the other keeps each list's working
+// set resident; both cases take two launches.
+int run_grads(const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
+  const double streamed = 4.0 * a.B * a.H * (double)a.N * d * (dtype == FA_BF16 ? 2 : 4);
+  const bool uneven = causal || a.seqlens != nullptr;
+  if (uneven && streamed <= 128.0 * (1 << 20)) return run_stage(kGrads, a, d, dtype, causal, stream);
+  const int st = run_stage(kDkDv, a, d, dtype, causal, stream);
+  if (st != FA_OK) return st;
+  return run_stage(kDq, a, d, dtype, causal, stream);
+}
+
 }  // namespace
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
@@ -103,7 +120,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (st != FA_OK) return st;
   st = run_stage(kPrepare, a, d, dtype, causal, stream);
   if (st != FA_OK) return st;
-  return run_stage(kGrads, a, d, dtype, causal, stream);
+  return run_grads(a, d, dtype, causal, stream);
 }
 
 int fa_bwd_prepare(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -146,7 +163,7 @@ int fa_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dO, 
                      dtype, kGrads, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
-  return run_stage(kGrads, a, d, dtype, causal, stream);
+  return run_grads(a, d, dtype, causal, stream);
 }
 
 const char* fa_status_string(int status) {

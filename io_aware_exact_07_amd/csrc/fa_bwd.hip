@@ -177,8 +177,9 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
       dma16(src, rst(STG));
     }
   };
-  if (qb_begin < qb_end) issue(qb_begin, std::integral_constant<int, 0>());
-  if (qb_begin + 1 < qb_end) issue(qb_begin + 1, std::integral_constant<int, 1>());
+  static_for<S - 1>([&](auto J) {
+    if (qb_begin + J < qb_end) issue(qb_begin + J, J);
+  });
 
   f32x16 dKacc[NDT], dVacc[NDT];
 #pragma unroll
@@ -194,15 +195,11 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
   auto block = [&](const int qb, auto STG) {
     constexpr int buf = decltype(STG)::value;
     constexpr int nxt = (buf + S - 1) % S;
-    // Block qb has landed once at most the next block's copies are pending.
-    if (qb + 1 < qb_end) {
-      if (w == 0) __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_WAVE0));
-      else __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_OTHERS));
-    } else {
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
-    }
+    // Block qb has landed once at most the later blocks' copies are pending.
+    if (w == 0) wait_blocks<S - 2, VM_WAVE0>(qb_end - 1 - qb);
+    else wait_blocks<S - 2, VM_OTHERS>(qb_end - 1 - qb);
     barrier_lds();  // block qb visible to all waves; stage nxt no longer read
-    if (qb + 2 < qb_end) issue(qb + 2, std::integral_constant<int, nxt>());
+    if (qb + S - 1 < qb_end) issue(qb + S - 1, std::integral_constant<int, nxt>());
     const int q0 = qb * BQ;
     const T* Qs = qst(STG);
     const T* dOs = ost(STG);
@@ -210,8 +207,10 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
     // Masking is needed only where the block crosses the diagonal of this
     // wave's keys or the wave holds padded keys (padded query rows carry
     // lse2 = +inf and D = 0).
-    const bool edge = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > L);
-
+    // The two versions of the tile loop keep the masking branch out of the
+    // loop body, so the scheduler can overlap one tile's matrix products with
+    // the other tile's exponentials.
+    auto tiles = [&](auto EDGE) {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
       f32x16 s = zero16(), dp = zero16();
@@ -220,7 +219,7 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
         mma16(s, fr.row(Qs, qt, c), kf[c]);
         mma16(dp, fr.row(dOs, qt, c), vf[c]);
       }
-      if (edge) {
+      if constexpr (decltype(EDGE)::value) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qq = q0 + 32 * qt + acc_row(i, h);
@@ -257,12 +256,14 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
           mma16(dKacc[t], dsf[cc], fr.col(Qs, 32 * qt + 16 * cc, t));
         }
     }
+    };
+    if ((CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > L)) tiles(std::true_type());
+    else tiles(std::false_type());
   };
-  for (int qb = qb_begin; qb < qb_end; qb += S) {
-    block(qb, std::integral_constant<int, 0>());
-    if (qb + 1 < qb_end) block(qb + 1, std::integral_constant<int, 1>());
-    if (qb + 2 < qb_end) block(qb + 2, std::integral_constant<int, 2>());
-  }
+  for (int qb = qb_begin; qb < qb_end; qb += S)
+    static_for<S>([&](auto J) {
+      if (qb + J < qb_end) block(qb + J, J);
+    });
 
   // dV / dK tiles: lane = head-dim column, registers = keys.
 #pragma unroll
@@ -306,10 +307,6 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
   constexpr int S = SH::S;
   auto kst = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE); };
   auto vst = [&](auto STG) -> T* { return reinterpret_cast<T*>(lds + decltype(STG)::value * SH::STAGE + SH::TILE); };
-  T* sK0 = kst(std::integral_constant<int, 0>());
-  T* sV0 = vst(std::integral_constant<int, 0>());
-  T* sK1 = kst(std::integral_constant<int, 1>());
-  T* sV1 = vst(std::integral_constant<int, 1>());
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int b = bh / a.H;
@@ -357,47 +354,53 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
     dma.issue(Kg, kb * BK, a.N, kd, tid);
     dma.issue(Vg, kb * BK, a.N, vd, tid);
   };
-  if (0 < nkb) issue(0, sK0, sV0);
-  if constexpr (S > 2) {
-    if (1 < nkb) issue(1, sK1, sV1);
-  }
+  static_for<S - 1>([&](auto J) {
+    if (J < nkb) issue(J, kst(J), vst(J));
+  });
   // One key/value block from pipeline stage STG (compile-time, so every LDS
   // address is a precomputed per-lane offset plus an immediate).
   auto block = [&](const int kb, auto STG) {
     constexpr int buf = decltype(STG)::value;
     constexpr int nxt = (buf + S - 1) % S;
-    if (kb + S - 2 < nkb)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_PER_BLOCK * (S - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+    wait_blocks<S - 2, VM_PER_BLOCK>(nkb - 1 - kb);
     barrier_lds();  // block kb visible to all waves; stage nxt no longer read
     if (kb + S - 1 < nkb) issue(kb + S - 1, kst(std::integral_constant<int, nxt>()), vst(std::integral_constant<int, nxt>()));
     const int k0 = kb * BK;
     if (!(wave_live && k0 < kend_w)) return;
     const T* kt = kst(STG);
     const T* vt = vst(STG);
-    f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+    // Two versions of the block body keep the masking branch out of it, so
+    // the scheduler can overlap one tile's exponentials with the other
+    // tile's matrix products.
+    auto body = [&](auto EDGE) {
+    constexpr int NKT = BK / 32;  // 32-key tiles per block
+    f32x16 s[NKT], dp[NKT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NKT; ++t) {
+      s[t] = zero16();
+      dp[t] = zero16();
+    }
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         mma16(s[t], fr.row(kt, t, c), qf[c]);
         mma16(dp[t], fr.row(vt, t, c), df[c]);
       }
     // Masked scores become -inf (probability exactly 0); only blocks that
-    // cross the padding boundary or the diagonal take this branch.
-    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
+    // cross the padding boundary or the diagonal take this version.
+    if constexpr (decltype(EDGE)::value) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NKT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * t + acc_row(i, h);
           if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
         }
     }
-    Frag<T> dsf[4];
+    Frag<T> dsf[2 * NKT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
@@ -406,15 +409,15 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mma16(acc[t], fr.col(kt, 16 * c, t), dsf[c]);
+      for (int c = 0; c < 2 * NKT; ++c) mma16(acc[t], fr.col(kt, 16 * c, t), dsf[c]);
+    };
+    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) body(std::true_type());
+    else body(std::false_type());
   };
-  for (int kb = 0; kb < nkb; kb += S) {
-    block(kb, std::integral_constant<int, 0>());
-    if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>());
-    if constexpr (S > 2) {
-      if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>());
-    }
-  }
+  for (int kb = 0; kb < nkb; kb += S)
+    static_for<S>([&](auto J) {
+      if (kb + J < nkb) block(kb + J, J);
+    });
 
   if (qrow < a.N) {
     const float sc = row_ok ? a.scale : 0.f;

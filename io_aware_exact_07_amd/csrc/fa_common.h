@@ -16,6 +16,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 #include <stdint.h>
 
 namespace fa {
@@ -366,6 +367,30 @@ __device__ __forceinline__ void barrier_lds() {
 
 // s_waitcnt immediate for vmcnt(n) (n < 64) with expcnt and lgkmcnt unconstrained.
 __device__ __forceinline__ constexpr int wait_vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Waits until at most min(K, avail) blocks of PER copy instructions each are
+// still pending for this wave (vmcnt takes an immediate, so the run-time
+// count selects among the compile-time ones).
+template <int K, int PER>
+__device__ __forceinline__ void wait_blocks(int avail) {
+  if constexpr (K <= 0) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+  } else {
+    static_assert(K * PER < 64, "vmcnt holds at most 63");
+    if (avail >= K) __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(K * PER));
+    else wait_blocks<K - 1, PER>(avail);
+  }
+}
+
+// f(std::integral_constant<int, J>()) for J = 0 .. N-1, unrolled.
+template <int N, typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>());
+}
 
 __device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int N) {
   if (!seqlens) return N;

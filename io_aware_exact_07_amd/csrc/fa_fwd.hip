@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   // Each stage is its own LDS array so the compiler can tell that copies
   // into one stage never alias reads of another.
   constexpr int S = (sizeof(T) == 2 && D == 64) ? 3 : 2;
+  static_assert(S >= 2 && S <= 3, "two or three pipeline stages");
   constexpr int TS = BK * D, TS2 = S > 2 ? BK * D : 8;
   __shared__ __attribute__((aligned(16))) T sK0[TS];  // swizzled Tile<T, D> layout
   __shared__ __attribute__((aligned(16))) T sV0[TS];
@@ -121,20 +122,16 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
     dma.issue(K, kb * BK, a.N, kd, tid);
     dma.issue(V, kb * BK, a.N, vd, tid);
   };
-  if (0 < nkb) issue(0, sK0, sV0);
-  if constexpr (S > 2) {
-    if (1 < nkb) issue(1, sK1, sV1);
-  }
+  static_for<S - 1>([&](auto J) {
+    if (J < nkb) issue(J, kst(J), vst(J));
+  });
   // One key/value block from pipeline stage STG (compile-time, so every LDS
   // address below is a precomputed per-lane offset plus an immediate).
   auto block = [&](const int kb, auto STG) {
     constexpr int buf = decltype(STG)::value;
     constexpr int nxt = (buf + S - 1) % S;
     // Block kb has landed once at most the later blocks' copies are pending.
-    if (kb + S - 2 < nkb)
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(VM_PER_BLOCK * (S - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(0));
+    wait_blocks<S - 2, VM_PER_BLOCK>(nkb - 1 - kb);
     barrier_lds();  // block kb visible to all waves; stage nxt no longer read
     if (kb + S - 1 < nkb) issue(kb + S - 1, kst(std::integral_constant<int, nxt>()), vst(std::integral_constant<int, nxt>()));
     const int k0 = kb * BK;
@@ -200,13 +197,10 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
 #pragma unroll
       for (int c = 0; c < 4; ++c) mma16(acc[t], fr.col(vt, 16 * c, t), pf[c]);
   };
-  for (int kb = 0; kb < nkb; kb += S) {
-    block(kb, std::integral_constant<int, 0>());
-    if (kb + 1 < nkb) block(kb + 1, std::integral_constant<int, 1>());
-    if constexpr (S > 2) {
-      if (kb + 2 < nkb) block(kb + 2, std::integral_constant<int, 2>());
-    }
-  }
+  for (int kb = 0; kb < nkb; kb += S)
+    static_for<S>([&](auto J) {
+      if (kb + J < nkb) block(kb + J, J);
+    });
 
   const float ltot = pair_sum(lsum);
   if (qrow < a.N) {

@@ -112,8 +112,9 @@ def test_workspace_and_memory_are_linear_in_N():
 
 
 def test_separate_and_fused_gradient_stages_agree_bitwise():
-    """fa_bwd (prepare + one fused dK/dV/dQ launch) equals prepare + dkdv + dq."""
-    for causal, seqlens in ((True, None), (False, [300, 77])):
+    """fa_bwd (prepare, then one interleaved launch under the causal mask or with
+    seqlens, two launches otherwise) equals prepare + dkdv + dq."""
+    for causal, seqlens in ((True, None), (False, [300, 77]), (False, None)):
         inp = W.random_inputs(2, 3, 300, 64, "bf16", seed=21, gain=1.5, seqlens=seqlens)
         q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
         sl = None if inp["seqlens"] is None else inp["seqlens"].to(DEV)

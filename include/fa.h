@@ -76,7 +76,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs: two float32 row vectors per head,
- * D_i = dO_i . o_i and lse_i * log2(e), each holding N rounded up to a
+ * -D_i (D_i = dO_i . o_i) and lse_i * log2(e), each holding N rounded up to a
  * multiple of 128 rows per head (the padding rows are written too), each
  * rounded up to 256 bytes.  Linear in N.  Returns 0 for empty or invalid
  * shapes.
@@ -103,7 +103,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * schedule them themselves.  fa_bwd is prepare followed by dkdv_dq; prepare
  * followed by dkdv and dq (in either order, or on two streams ordered after
  * prepare) computes the same, bit for bit.
- *   prepare: D_i = dO_i . o_i and lse_i in base 2 into the workspace (reads
+ *   prepare: -D_i (D_i = dO_i . o_i) and lse_i in base 2 into the workspace (reads
  *            o, dO, lse).  A row of the softmax-Jacobian product reduces to
  *            dS_ij = P_ij (dP_ij - D_i) because sum_j P_ij dP_ij = dO_i . o_i.
  *   dkdv:    recomputes the score blocks key block by key block and writes

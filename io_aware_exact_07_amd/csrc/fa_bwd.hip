@@ -35,7 +35,7 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
 // 1. Row vectors for the gradient stages, over Npad rows per head:
-//    delta[i] = dO_i . o_i and lse2[i] = lse_i * log2(e) for rows i < L;
+//    delta[i] = -(dO_i . o_i) and lse2[i] = lse_i * log2(e) for rows i < L;
 //    delta = 0 and lse2 = +inf (every probability of the row 0) for padded
 //    rows and for the rows that round the head up to whole 128-row blocks.
 //    CPR threads cooperate on one row.
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, CPR);
     if (prow < rows && part == 0) {
-      a.delta[prow] = in ? dot : 0.f;
+      a.delta[prow] = in ? -dot : 0.f;  // stored negated: the dP products accumulate onto it
       a.lse2[prow] = in ? a.lse[bh * a.N + pos] * kLog2e : INFINITY;
     }
   }
@@ -213,7 +213,14 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
     auto tiles = [&](auto EDGE) {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-      f32x16 s = zero16(), dp = zero16();
+      // dP starts from -D of each query row, so the product leaves dP - D.
+      f32x16 s = zero16(), dp;
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Rs + BQ + 32 * qt + 8 * gi + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * gi + j] = d4[j];
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         mma16(s, fr.row(Qs, qt, c), kf[c]);
@@ -230,12 +237,11 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(Rs + 32 * qt + 8 * gi + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Rs + BQ + 32 * qt + 8 * gi + 4 * h);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * gi + j;
           p[i] = exp2_fast(fmaf(s[i], c2, -l4[j]));
-          ds[i] = p[i] * (dp[i] - d4[j]);
+          ds[i] = p[i] * dp[i];
         }
       }
       // Registers 8cc..8cc+7 enumerate queries 16cc..16cc+15 of this tile in
@@ -336,7 +342,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
   }
   // Padded and past-the-end rows carry lse2 = +inf (every probability 0), D = 0.
   const float lse2 = a.lse2[roff + qrow];
-  const float dq_i = a.delta[roff + qrow];
+  const float ndq_i = a.delta[roff + qrow];  // -D of this lane's query
   const float c2 = a.scale * kLog2e;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -404,7 +410,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
-        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] - dq_i));
+        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] + ndq_i));
       }
 #pragma unroll
     for (int t = 0; t < NDT; ++t)

@@ -28,7 +28,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* lse2;     // float32 [B*H][Npad] scratch: lse_i * log2(e), +inf for rows >= L
-  float* delta;    // float32 [B*H][Npad] scratch: D_i = dO_i . o_i, 0 for rows >= L
+  float* delta;    // float32 [B*H][Npad] scratch: -D_i = -(dO_i . o_i), 0 for rows >= L
   const int32_t* seqlens;
   int B, H, N;
   float scale;

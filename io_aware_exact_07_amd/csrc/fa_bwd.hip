@@ -343,6 +343,11 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
   // Padded and past-the-end rows carry lse2 = +inf (every probability 0), D = 0.
   const float lse2 = a.lse2[roff + qrow];
   const float ndq_i = a.delta[roff + qrow];  // -D of this lane's query
+  // dP^T starts from -D (every register of a lane is the same query), so the
+  // product leaves dP - D; the copy is loop-invariant.
+  f32x16 ndq16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndq16[i] = ndq_i;
   const float c2 = a.scale * kLog2e;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -384,7 +389,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
       s[t] = zero16();
-      dp[t] = zero16();
+      dp[t] = ndq16;
     }
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
@@ -410,7 +415,7 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
-        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * (dp[t][i] + ndq_i));
+        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * dp[t][i]);
       }
 #pragma unroll
     for (int t = 0; t < NDT; ++t)

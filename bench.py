@@ -30,6 +30,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                             causal attention stack, N = 512..32768, vs the
                                             recomputation page's model and explicit attention)
        python bench.py --compare-explicit  (JSON lines: fwd+bwd time vs explicit attention)
+       python bench.py --sweep             (JSON lines: causal H=12 d=64, N = 1k..32k, B = 16384/N)
 """
 from __future__ import annotations
 
@@ -218,6 +219,42 @@ def compare_explicit(steps=10):
         torch.cuda.empty_cache()
 
 
+def sweep(steps=20, warmup=5):
+    """fwd+bwd rate over sequence lengths at a fixed token count: H=12, d=64,
+    causal, N = 1k .. 32k, B = 16384 / N (B = 1 at N = 32k; one JSON line per N)."""
+    import torch
+    import io_aware_exact_07_amd as fa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    for N in (1024, 2048, 4096, 8192, 16384, 32768):
+        B = max(1, 16384 // N)  # N = 32k: one sequence
+        w = W.Workload(f"causal sweep B={B} H=12 N={N} d=64", B, 12, N, 64, "bf16", True, 5)
+        inp = W.make_inputs(w)
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+
+        def step():
+            o, lse = fa.forward(q, k, v, causal=True)
+            fa.backward(q, k, v, o, do, lse, causal=True)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        f_fwd, f_bwd = w.flops()
+        print(json.dumps({"mode": "sweep", "workload": w.name, "B": B, "N": N, "ms_per_step": round(ms, 5),
+                          "tflops": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 3),
+                          "pct_peak": round(100 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}),
+              flush=True)
+        del q, k, v, do
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, min_seconds=10.0):
     """The oracle as it stands, on whole heads of the workload (as many as fit
     in about min_seconds, at least one), on this host's cores."""
@@ -240,7 +277,19 @@ def cpu_baseline(w, min_seconds=10.0):
     dt = time.perf_counter() - t0
     f_fwd, f_bwd = w.flops()
     flops = (f_fwd + f_bwd) * done / len(heads)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info() if i.get("user_api") == "blas"}))
+    except Exception:
+        blas = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"{done} of {len(heads)} heads of the same workload, full forward + backward in float64 "
                       f"numpy; {dt:.2f} s for {flops / 1e9:.1f} counted GFLOP"}
 
@@ -256,6 +305,8 @@ def main():
                     help="peak memory of a 12-layer causal attention stack vs the page's model")
     ap.add_argument("--compare-explicit", action="store_true",
                     help="time the tiled path against explicit attention")
+    ap.add_argument("--sweep", action="store_true",
+                    help="JSON lines: causal H=12 d=64 at N = 1k..32k with B = 16384/N")
     ap.add_argument("--workload", default="gpt2_long", choices=sorted(WORKLOAD_KEYS),
                     help="which synthetic workload a step runs (default: the long-context GPT-2 head)")
     ap.add_argument("--head-dim", type=int, default=None,
@@ -275,6 +326,9 @@ def main():
     if args.compare_explicit:
         compare_explicit()
         return
+    if args.sweep:
+        sweep()
+        return
 
     import torch
     import io_aware_exact_07_amd as fa
@@ -282,7 +336,7 @@ def main():
 
     w = getattr(W, WORKLOAD_KEYS[args.workload])
     if args.head_dim is not None and args.head_dim != w.d:
-        w = dataclasses.replace(w, d=args.head_dim, name=f"{w.name} (head dimension {args.head_dim})", scale=None)
+        w = dataclasses.replace(w, d=args.head_dim, name=w.name.replace(f"d={w.d}", f"d={args.head_dim}"), scale=None)
     default_workload = args.workload == "gpt2_long" and w.d == W.GPT2_LONG.d
     dev = torch.device("cuda:0")
     inp = W.make_inputs(w)
@@ -369,6 +423,8 @@ def main():
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
         "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv_dq": round(grads_ms, 5)},
+        "effective_tflops": (round(value * float((sl.double() ** 2).sum()) / (B * N * N), 3) if sl is not None
+                             else None),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
         "pct_peak": round(100.0 * value / peak, 2),

@@ -306,12 +306,36 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
 }
 #pragma clang diagnostic pop
 
+// One global_load_lds_dwordx4 in its scalar-base form: every active lane
+// copies the 16 bytes at base + off (base wave-uniform in SGPRs, off a
+// 32-bit per-lane byte offset) to LDS address m0 + 16 * lane.  Same
+// synchronisation contract as dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16s(const void* base, unsigned off, unsigned m0) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(m0), "v"(off), "s"(base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
+}
+
 // Direct HBM -> LDS copy (global_load_lds_dwordx4) of rows [r0, r0+R) of a
 // row-major [nrows][D] array into a swizzled Tile<T, D>.  Each instruction
 // moves 64 lanes x 16 bytes into a contiguous 1 KB span of LDS (lane l
 // writes bytes 16l..16l+15 of the span), so lane l of wave w, instruction u,
 // fills physical chunk P = (u*NW + w)*64 + l and loads the global chunk that
-// the swizzle maps there.  Rows >= nrows re-read row nrows-1 (finite data the
+// the swizzle maps there.  The source is addressed as a scalar row base plus
+// a loop-invariant per-lane byte offset, so a block's copies cost no vector
+// address arithmetic.  Rows >= nrows re-read row nrows-1 (finite data the
 // kernels mask out).  Completion is tracked by the wave's vmcnt; the data is
 // visible to other waves after a workgroup barrier.
 template <typename T, int R, int D, int NT>
@@ -319,35 +343,35 @@ struct TileDma {
   static constexpr int EPC = 16 / sizeof(T);
   static constexpr int CPR = D / EPC;
   static constexpr int NW = NT / 64;
+  static constexpr int RB = D * (int)sizeof(T);  // bytes per row
   static constexpr int TOTAL = R * CPR;
   static_assert(TOTAL % NT == 0, "tile must split evenly over the threads");
   static constexpr int PER = TOTAL / NT;  // instructions per thread per tile
-  int gofs[PER];                          // element offset of this lane's chunk in rows r0..
+  unsigned voff[PER];                     // byte offset of this lane's chunk from row r0
   int prow[PER];                          // tile row of that chunk
+  int wu;                                 // wave index, wave-uniform
   __device__ __forceinline__ void init(int tid) {
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    wu = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int P = (u * NW + w) * 64 + lane;
+      const int P = (u * NW + wu) * 64 + lane;
       const int row = P / CPR, pc = P % CPR;
       prow[u] = row;
-      gofs[u] = row * D + Tile<T, D>::logical(row, pc) * EPC;
+      voff[u] = (unsigned)(row * RB + Tile<T, D>::logical(row, pc) * 16);
     }
   }
-  __device__ __forceinline__ void issue(const T* g, int r0, int nrows, T* lds, int tid) const {
-    const int w = tid >> 6;
+  // Requires r0 < nrows.
+  __device__ __forceinline__ void issue(const T* g, int r0, int nrows, const T* lds, int /*tid*/) const {
+    const char* base = reinterpret_cast<const char*>(g) + (size_t)r0 * RB;
+    const unsigned dst = lds_addr(lds);
     const bool inside = r0 + R <= nrows;
+    const int last = nrows - 1 - r0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const T* src;
-      if (inside) {
-        src = g + (size_t)r0 * D + gofs[u];
-      } else {
-        const int gr = min(r0 + prow[u], nrows - 1);
-        src = g + (size_t)gr * D + (gofs[u] - prow[u] * D);
-      }
-      T* dst = lds + (u * NW + w) * 64 * EPC;
-      dma16(src, dst);
+      unsigned off = voff[u];
+      if (!inside) off -= (unsigned)((prow[u] - min(prow[u], last)) * RB);
+      dma16s(base, off, dst + (unsigned)((u * NW + wu) * 64 * 16));
     }
   }
 };

@@ -149,3 +149,30 @@ def test_long_context_sampled(w, nheads_rows, nkeys):
     say(f"  key rows checked {time.time() - t0:.1f}s dk {e_dk:.3e} dv {e_dv:.3e}")
     assert e_dk <= tol["dk"] and e_dv <= tol["dv"]
     check_invariants(inp, got, w)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_ragged_length_sampled(d):
+    """A length far past the workloads and off every block size (N = 100003,
+    prime), causal: 128 random query rows per head against the oracle, plus the
+    dK/dV invariants and the exact first row."""
+    N = 100003
+    w = W.Workload(f"ragged long B=1 H=2 N={N} d={d} causal", 1, 2, N, d, "bf16", True, 7)
+    say(f"workload {w.name}")
+    inp = W.make_inputs(w)
+    t0 = time.time()
+    got = gpu_run(inp, True, w.softmax_scale)
+    say(f"  gpu done {time.time() - t0:.1f}s")
+    tol = TOL["bf16"]
+    rng = np.random.default_rng(11)
+    rows = np.sort(np.concatenate([rng.choice(N - 200, 120, replace=False), np.arange(N - 8, N)]))
+    errs = dict(o=0.0, dq=0.0, lse=0.0)
+    for h in range(w.H):
+        q64, k64, v64, do64 = (f64(inp[n][0, h]) for n in ("q", "k", "v", "do"))
+        O, lse, dq = oracle.rows_forward_backward(q64, k64, v64, do64, w.softmax_scale, rows, True)
+        errs["o"] = max(errs["o"], rel_err(f64(got["o"][0, h])[rows], O))
+        errs["dq"] = max(errs["dq"], rel_err(f64(got["dq"][0, h])[rows], dq))
+        errs["lse"] = max(errs["lse"], lse_err(f64(got["lse"][0, h])[rows], lse))
+    say(f"  rows checked {time.time() - t0:.1f}s errs {errs}")
+    assert errs["o"] <= tol["o"] and errs["dq"] <= tol["dq"] and errs["lse"] <= tol["lse"], errs
+    check_invariants(inp, got, w)

@@ -89,8 +89,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 template <typename T, int D>
 struct DkdvShape {
   static constexpr int BK = 128;
-  static constexpr int BQ = (sizeof(T) == 4 && D > 64) ? 32 : 64;  // fp32 d=96, 128 keep their registers
-  static constexpr int S = 3;                                        // pipeline stages
+  // Query rows per block and pipeline stages.  bf16 d=64 takes 128-row
+  // blocks (half the barriers per score tile) in two stages, which still
+  // fits two workgroups per CU; fp32 d=96, 128 take 32 rows to keep their
+  // registers.
+  static constexpr bool WIDE = sizeof(T) == 2 && D == 64;
+  static constexpr int BQ = WIDE ? 128 : (sizeof(T) == 4 && D > 64) ? 32 : 64;
+  static constexpr int S = WIDE ? 2 : 3;
+  static_assert(BQ / 2 <= 64, "one wave copies a block's lse2 and -D rows, 4 floats per lane");
   static constexpr int TILE = BQ * D * (int)sizeof(T);               // bytes of one Q or dO tile
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;                // Q, dO, lse2 | D
   static constexpr int LDS = S * STAGE;

@@ -405,6 +405,7 @@ def main():
     compulsory += e * 4 * B * H * N * d + 8 * B * H * N                # gradients: q, k, v, dO, lse2, D in
     compulsory += e * 3 * B * H * N * d                                # dk, dv, dq out
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    traffic = recorded_traffic(dom) if default_workload else None
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -436,7 +437,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": recorded_traffic(dom) if default_workload else None,
+            "traffic": traffic,
+            "traffic_gbs": None if traffic is None else round(traffic / (launches[dom] * 1e-3) / 1e9, 1),
             "avg_launch_ms": round(launches[dom], 5),
         },
     }

@@ -4,6 +4,7 @@ Small cases are compared element by element over every output; the five
 full-size workloads are compared on sampled outputs the oracle can compute
 (whole heads, query rows, key rows) plus properties that hold at any size.
 """
+import dataclasses
 import math
 import os
 import sys
@@ -120,7 +121,12 @@ def check_invariants(inp, got, w):
         assert torch.equal(got["o"][:, :, 0], inp["v"][:, :, 0])
 
 
-@pytest.mark.parametrize("w,nheads_rows,nkeys", [(W.GPT2_LONG, 12, 256), (W.VERY_LONG, 16, 256)])
+@pytest.mark.parametrize("w,nheads_rows,nkeys", [
+    (W.GPT2_LONG, 12, 256),
+    (W.VERY_LONG, 16, 256),
+    # head dimension 96 at the long-context shape (same recipe and seed)
+    (dataclasses.replace(W.GPT2_LONG, d=96, name="GPT-2 head long context B=1 H=12 N=8192 d=96 causal, QK x2"), 12, 128),
+])
 def test_long_context_sampled(w, nheads_rows, nkeys):
     """256 random query rows in every head (O, LSE, dQ) and 256 random key rows
     of one head (dK, dV, streaming all queries through the oracle)."""

@@ -7,21 +7,21 @@
 // Recomputed"; dmarx anthology record SOTA-087, "Why recomputation is cheaper
 // here than storing").
 //
-// Three kernels on one stream:
-//   1. bwd_pre:  D_i = dO_i . o_i (float32).  Because each row of the softmax
-//      Jacobian satisfies sum_j P_ij dP_ij = dO_i . o_i, the Jacobian
+// Two kernels on one stream:
+//   1. bwd_pre:  -D_i = -(dO_i . o_i) (float32).  Because each row of the
+//      softmax Jacobian satisfies sum_j P_ij dP_ij = dO_i . o_i, the Jacobian
 //      product collapses to dS_ij = P_ij (dP_ij - D_i).
-//   2. bwd_dkdv: one workgroup keeps a block of 128 keys (K_j, V_j) resident
-//      and sweeps the query blocks, recomputing S = Q K^T and dP = dO V^T and
-//      accumulating dV += P^T dO and dK += dS^T Q in registers.
-//   3. bwd_dq:   one workgroup keeps a block of 128 queries resident and sweeps
-//      the key blocks, recomputing S and dP once more and accumulating
-//      dQ += dS K in registers.
-// dQ is reduced by this separate pass, not by float atomics from stage 2:
-// device-scope float atomics are resolved beyond the per-XCD L2 caches, and
-// at 4 bytes per (key block, query, dim) their request rate, not the two
-// extra matrix products per score block, bounds the pass.  Stages 2 and 3
-// are independent once D exists.  Everything is deterministic.
+//   2. bwd_grad: two lists of blocks.  A dK/dV block keeps 128 keys (K_j, V_j)
+//      resident and sweeps the query blocks, recomputing S = Q K^T and
+//      dP = dO V^T and accumulating dV += P^T dO and dK += dS^T Q in
+//      registers.  A dQ block keeps 128 queries resident and sweeps the key
+//      blocks, recomputing S and dP once more and accumulating dQ += dS K in
+//      registers.  One launch runs either list alone or both interleaved.
+// dQ is reduced by its own block list, not by float atomics from the dK/dV
+// blocks: device-scope float atomics are resolved beyond the per-XCD L2
+// caches, and at 4 bytes per (key block, query, dim) their request rate, not
+// the two extra matrix products per score block, bounds the pass.  The two
+// lists are independent once D exists.  Everything is deterministic.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // tiles, so a lane owns one key and holds 16 queries of a tile in registers.
 // P and dS then feed dV += P^T dO and dK += dS^T Q straight from registers
 // (the contraction runs over the queries held in-register; dO and Q are read
-// as column fragments in the matching order).  Query blocks are double
-// buffered: the next block's Q, dO, lse and D are fetched into registers
-// while the current one is computed, then parked in the idle buffer.
+// as column fragments in the matching order).  Query blocks stream through S
+// LDS stages filled by direct HBM -> LDS copies issued S-1 blocks ahead: the
+// Q and dO tiles, plus the block's lse2 and -D row vectors.
 template <typename T, int D>
 struct DkdvShape {
   static constexpr int BK = 128;

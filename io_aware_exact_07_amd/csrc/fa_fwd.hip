@@ -1,8 +1,9 @@
 // Forward pass of exact tiled attention on gfx950.
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-// owns 32 rows.  Key/value blocks of 64 rows are streamed through LDS
-// (double buffered, one barrier per block) and every block of scores lives
+// owns 32 rows.  Key/value blocks of 64 rows are streamed through LDS (a
+// pipeline of direct HBM -> LDS copies, one barrier per block) and every
+// block of scores lives
 // only in registers: it is produced by the matrix cores, folded into the
 // running max / normaliser / output accumulator, and dropped (dmarx anthology
 // record SOTA-087, "Why recomputation is cheaper here than storing": the score

@@ -307,8 +307,9 @@ struct DqShape {
 };
 
 // One query block (BQ queries of head bh): dQ.  `lds` holds S stages of
-// [K tile | V tile].
-template <typename T, int D, bool CAUSAL>
+// [K tile | V tile].  G = 32-key tiles whose scores are live at once: the
+// whole block, or one tile at a time where the register budget is halved.
+template <typename T, int D, bool CAUSAL, int G>
 __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const int bh, char* lds) {
   using SH = DqShape<T, D>;
   constexpr int BQ = SH::BQ, BK = SH::BK, NT = kThreads;
@@ -350,7 +351,10 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
   const float lse2 = a.lse2[roff + qrow];
   const float ndq_i = a.delta[roff + qrow];  // -D of this lane's query
   // dP^T starts from -D (every register of a lane is the same query), so the
-  // product leaves dP - D; the copy is loop-invariant.
+  // product leaves dP - D; the copy is loop-invariant.  At bf16 d>64 (only
+  // ever the dQ-only launch) the register budget has no room for it, and -D
+  // is added after the product instead.
+  constexpr bool NDQ_IN_MMA = !(sizeof(T) == 2 && D > 64);
   f32x16 ndq16;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ndq16[i] = ndq_i;
@@ -391,42 +395,46 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
     // tile's matrix products.
     auto body = [&](auto EDGE) {
     constexpr int NKT = BK / 32;  // 32-key tiles per block
-    f32x16 s[NKT], dp[NKT];
+    static_assert(NKT % G == 0, "tile groups must divide the block");
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-      s[t] = zero16();
-      dp[t] = ndq16;
-    }
+    for (int g0 = 0; g0 < NKT; g0 += G) {
+      f32x16 s[G], dp[G];
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        mma16(s[t], fr.row(kt, t, c), qf[c]);
-        mma16(dp[t], fr.row(vt, t, c), df[c]);
+      for (int t = 0; t < G; ++t) {
+        s[t] = zero16();
+        dp[t] = NDQ_IN_MMA ? ndq16 : zero16();
       }
-    // Masked scores become -inf (probability exactly 0); only blocks that
-    // cross the padding boundary or the diagonal take this version.
-    if constexpr (decltype(EDGE)::value) {
 #pragma unroll
-      for (int t = 0; t < NKT; ++t)
+      for (int t = 0; t < G; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          mma16(s[t], fr.row(kt, g0 + t, c), qf[c]);
+          mma16(dp[t], fr.row(vt, g0 + t, c), df[c]);
+        }
+      // Masked scores become -inf (probability exactly 0); only blocks that
+      // cross the padding boundary or the diagonal take this version.
+      if constexpr (decltype(EDGE)::value) {
+#pragma unroll
+        for (int t = 0; t < G; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * (g0 + t) + acc_row(i, h);
+            if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
+          }
+      }
+      Frag<T> dsf[2 * G];
+#pragma unroll
+      for (int t = 0; t < G; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * t + acc_row(i, h);
-          if (key >= L || (CAUSAL && key > qrow)) s[t][i] = -INFINITY;
+          const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
+          dsf[2 * t + (i >> 3)][i & 7] = (T)(NDQ_IN_MMA ? p * dp[t][i] : p * (dp[t][i] + ndq_i));
         }
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int c = 0; c < 2 * G; ++c) mma16(acc[t], fr.col(kt, 32 * g0 + 16 * c, t), dsf[c]);
     }
-    Frag<T> dsf[2 * NKT];
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(fmaf(s[t][i], c2, -lse2));
-        dsf[2 * t + (i >> 3)][i & 7] = (T)(p * dp[t][i]);
-      }
-#pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-      for (int c = 0; c < 2 * NKT; ++c) mma16(acc[t], fr.col(kt, 16 * c, t), dsf[c]);
     };
     if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) body(std::true_type());
     else body(std::false_type());
@@ -448,16 +456,36 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 }
 
 // ---------------------------------------------------------------------------
+// Waves per SIMD the register budget targets: two at bf16 d=64, and for a
+// dQ-only launch at bf16 d>64, whose body then holds one 32-key tile's scores
+// at a time to fit 256 registers; one otherwise.
+template <typename T, int D, int MODE>
+constexpr int grad_occupancy() {
+  return (sizeof(T) == 2 && (D == 64 || MODE == 2)) ? 2 : 1;
+}
+
+// Whether the interleaved launch (MODE 0) exists.  At bf16 d>64 it would run
+// both bodies at one wave per SIMD, while the dQ-only launch runs two; the two
+// single-list launches in a row measure faster there, and take its place.
+template <typename T, int D>
+constexpr bool fused_grads() {
+  return !(sizeof(T) == 2 && D > 64);
+}
+
 // Gradient kernel.  MODE 1: dK/dV blocks only; MODE 2: dQ blocks only;
 // MODE 0: both job lists in one launch.  With a causal mask the work of a
 // block ranges from one block-step to N/64, and a lone launch of either list
 // has its heaviest blocks longer than the average per resident workgroup.
 // Interleaving the two independent lists heaviest-first (rank r of each list
 // in turn, every head) doubles the work per slot so the greedy dispatch
-// balances it.  Both bodies share one LDS allocation.
+// balances it.  In MODE 0 both bodies share one LDS allocation; a single-list
+// launch takes only its own body's, so a dQ-only launch is not held to the
+// footprint of the dK/dV stages.
 template <typename T, int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void bwd_grad_kernel(BwdArgs a) {
-  constexpr int LDS = DkdvShape<T, D>::LDS > DqShape<T, D>::LDS ? DkdvShape<T, D>::LDS : DqShape<T, D>::LDS;
+__global__ __launch_bounds__(kThreads, (grad_occupancy<T, D, MODE>())) void bwd_grad_kernel(BwdArgs a) {
+  constexpr int LDS = MODE == 1 ? DkdvShape<T, D>::LDS
+                      : MODE == 2 ? DqShape<T, D>::LDS
+                      : (DkdvShape<T, D>::LDS > DqShape<T, D>::LDS ? DkdvShape<T, D>::LDS : DqShape<T, D>::LDS);
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int BH = a.B * a.H;
   const int nb = (a.N + 127) / 128;  // 128-row blocks: key blocks of dK/dV, query blocks of dQ
@@ -472,7 +500,8 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 2 && D == 64) ? 2 : 1) void
   if (dkdv) {
     if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL>(a, rank, bh, lds);  // causal: low key blocks are heaviest
   } else {
-    if constexpr (MODE != 1) dq_block<T, D, CAUSAL>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
+    if constexpr (MODE != 1)
+      dq_block<T, D, CAUSAL, (grad_occupancy<T, D, MODE>() == 2 && D > 64) ? 1 : DqShape<T, D>::BK / 32>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
   }
 }
 
@@ -496,8 +525,12 @@ hipError_t launch_one(int stage, const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else if (stage == 3)
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    else
+    else if constexpr (fused_grads<T, D>())
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 0>), dim3((unsigned)(2 * grid)), dim3(kThreads), 0, stream, a);
+    else {
+      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

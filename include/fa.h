@@ -111,12 +111,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *   dq:      recomputes the score blocks query block by query block and
  *            writes dq (same inputs).
  *   dkdv_dq: both of the above.  With a causal mask or seqlens, up to
- *            128 MiB of streamed operands (4*B*H*N*d elements), and d = 64
- *            or float32, it is one launch that interleaves the two block
- *            lists heaviest first (a lone list's heaviest blocks outlast the
- *            average load of a resident workgroup); otherwise it is dkdv then
- *            dq on `stream` (at bf16 d > 64 the dq launch alone runs two
- *            waves per SIMD, which outweighs the interleaving).
+ *            128 MiB of streamed operands (4*B*H*N*d elements), and not
+ *            bf16 at d = 128, it is one launch that interleaves the two
+ *            block lists heaviest first (a lone list's heaviest blocks
+ *            outlast the average load of a resident workgroup); otherwise it
+ *            is dkdv then dq on `stream` (at bf16 d = 128 the dq launch alone
+ *            runs two waves per SIMD, which outweighs the interleaving).
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */

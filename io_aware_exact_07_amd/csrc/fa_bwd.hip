@@ -351,9 +351,9 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
   const float lse2 = a.lse2[roff + qrow];
   const float ndq_i = a.delta[roff + qrow];  // -D of this lane's query
   // dP^T starts from -D (every register of a lane is the same query), so the
-  // product leaves dP - D; the copy is loop-invariant.  At bf16 d>64 (only
-  // ever the dQ-only launch) the register budget has no room for it, and -D
-  // is added after the product instead.
+  // product leaves dP - D; the copy is loop-invariant.  At bf16 d>64 the
+  // two-wave register budget has no room for it, and -D is added after the
+  // product instead (in every launch mode, so they round alike).
   constexpr bool NDQ_IN_MMA = !(sizeof(T) == 2 && D > 64);
   f32x16 ndq16;
 #pragma unroll
@@ -456,20 +456,20 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 }
 
 // ---------------------------------------------------------------------------
-// Waves per SIMD the register budget targets: two at bf16 d=64, and for a
-// dQ-only launch at bf16 d>64, whose body then holds one 32-key tile's scores
-// at a time to fit 256 registers; one otherwise.
+// Waves per SIMD the register budget targets: two at bf16 d<=96 (the dQ body
+// then holds one 32-key tile's scores at a time when d>64) and for a dQ-only
+// launch at bf16 d=128; one otherwise.
 template <typename T, int D, int MODE>
 constexpr int grad_occupancy() {
-  return (sizeof(T) == 2 && (D == 64 || MODE == 2)) ? 2 : 1;
+  return (sizeof(T) == 2 && (D <= 96 || MODE == 2)) ? 2 : 1;
 }
 
-// Whether the interleaved launch (MODE 0) exists.  At bf16 d>64 it would run
+// Whether the interleaved launch (MODE 0) exists.  At bf16 d=128 it would run
 // both bodies at one wave per SIMD, while the dQ-only launch runs two; the two
 // single-list launches in a row measure faster there, and take its place.
 template <typename T, int D>
 constexpr bool fused_grads() {
-  return !(sizeof(T) == 2 && D > 64);
+  return !(sizeof(T) == 2 && D == 128);
 }
 
 // Gradient kernel.  MODE 1: dK/dV blocks only; MODE 2: dQ blocks only;

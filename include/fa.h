@@ -110,13 +110,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *            dk and dv (reads q, k, v, dO, lse and the prepared workspace).
  *   dq:      recomputes the score blocks query block by query block and
  *            writes dq (same inputs).
- *   dkdv_dq: both of the above.  With a causal mask or seqlens, up to
- *            128 MiB of streamed operands (4*B*H*N*d elements), and not
- *            bf16 at d = 128, it is one launch that interleaves the two
- *            block lists heaviest first (a lone list's heaviest blocks
- *            outlast the average load of a resident workgroup); otherwise it
- *            is dkdv then dq on `stream` (at bf16 d = 128 the dq launch alone
- *            runs two waves per SIMD, which outweighs the interleaving).
+ *   dkdv_dq: both of the above.  With a causal mask or seqlens, and up to
+ *            128 MiB of streamed operands (4*B*H*N*d elements), it is one
+ *            launch that interleaves the two block lists heaviest first (a
+ *            lone list's heaviest blocks outlast the average load of a
+ *            resident workgroup); otherwise it is dkdv then dq on `stream`.
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */

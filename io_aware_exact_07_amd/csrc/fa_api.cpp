@@ -98,8 +98,7 @@ int run_stage(int stage, const fa::BwdArgs& a, int d, int dtype, int causal, voi
 // is nothing to even out, and when the operands the two lists stream (Q, dO
 // and K, V of every head) no longer fit the 256 MB last-level cache
 // together, running the lists one after the other keeps each list's working
-// set resident; both cases take two launches.  So does bf16 at d=128, where
-// the kernels replace the interleaved launch by the two single-list ones.
+// set resident; both cases take two launches.
 int run_grads(const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
   const double streamed = 4.0 * a.B * a.H * (double)a.N * d * (dtype == FA_BF16 ? 2 : 4);
   const bool uneven = causal || a.seqlens != nullptr;

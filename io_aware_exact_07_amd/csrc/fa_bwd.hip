@@ -86,15 +86,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // as column fragments in the matching order).  Query blocks stream through S
 // LDS stages filled by direct HBM -> LDS copies issued S-1 blocks ahead: the
 // Q and dO tiles, plus the block's lse2 and -D row vectors.
-template <typename T, int D>
+template <typename T, int D, int OCC>
 struct DkdvShape {
   static constexpr int BK = 128;
   // Query rows per block and pipeline stages.  bf16 d=64 takes 128-row
   // blocks (half the barriers per score tile) in two stages, which still
   // fits two workgroups per CU; fp32 d=96, 128 take 32 rows to keep their
-  // registers.
+  // registers, and so does bf16 d=128 at OCC = 2 waves per SIMD.
   static constexpr bool WIDE = sizeof(T) == 2 && D == 64;
-  static constexpr int BQ = WIDE ? 128 : (sizeof(T) == 4 && D > 64) ? 32 : 64;
+  static constexpr int BQ = WIDE ? 128 : ((sizeof(T) == 4 && D > 64) || (D == 128 && OCC == 2)) ? 32 : 64;
   static constexpr int S = WIDE ? 2 : 3;
   static_assert(BQ / 2 <= 64, "one wave copies a block's lse2 and -D rows, 4 floats per lane");
   static constexpr int TILE = BQ * D * (int)sizeof(T);               // bytes of one Q or dO tile
@@ -104,9 +104,9 @@ struct DkdvShape {
 
 // One key block (BK keys of head bh): dK and dV.  `lds` holds S stages of
 // [Q tile | dO tile | lse2 | D].
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int OCC>
 __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const int bh, char* lds) {
-  using SH = DkdvShape<T, D>;
+  using SH = DkdvShape<T, D, OCC>;
   constexpr int BK = SH::BK, NT = kThreads;
   constexpr int BQ = SH::BQ;
   constexpr int NC = D / 16;
@@ -456,20 +456,14 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
 }
 
 // ---------------------------------------------------------------------------
-// Waves per SIMD the register budget targets: two at bf16 d<=96 (the dQ body
-// then holds one 32-key tile's scores at a time when d>64) and for a dQ-only
-// launch at bf16 d=128; one otherwise.
+// Waves per SIMD the register budget targets: two at bf16 (at d>64 the dQ
+// body then holds one 32-key tile's scores at a time, and at d=128 the dK/dV
+// body takes 32-row query blocks and spills a few registers), except for the
+// dK/dV-only launch at bf16 d=128, whose 64-row blocks run faster at one wave
+// with 256 VGPRs and 160 AGPRs.  One wave at fp32.
 template <typename T, int D, int MODE>
 constexpr int grad_occupancy() {
-  return (sizeof(T) == 2 && (D <= 96 || MODE == 2)) ? 2 : 1;
-}
-
-// Whether the interleaved launch (MODE 0) exists.  At bf16 d=128 it would run
-// both bodies at one wave per SIMD, while the dQ-only launch runs two; the two
-// single-list launches in a row measure faster there, and take its place.
-template <typename T, int D>
-constexpr bool fused_grads() {
-  return !(sizeof(T) == 2 && D == 128);
+  return (sizeof(T) == 2 && (D <= 96 || MODE != 1)) ? 2 : 1;
 }
 
 // Gradient kernel.  MODE 1: dK/dV blocks only; MODE 2: dQ blocks only;
@@ -483,9 +477,10 @@ constexpr bool fused_grads() {
 // footprint of the dK/dV stages.
 template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads, (grad_occupancy<T, D, MODE>())) void bwd_grad_kernel(BwdArgs a) {
-  constexpr int LDS = MODE == 1 ? DkdvShape<T, D>::LDS
-                      : MODE == 2 ? DqShape<T, D>::LDS
-                      : (DkdvShape<T, D>::LDS > DqShape<T, D>::LDS ? DkdvShape<T, D>::LDS : DqShape<T, D>::LDS);
+  constexpr int OCC = grad_occupancy<T, D, MODE>();
+  using KV = DkdvShape<T, D, OCC>;
+  using QS = DqShape<T, D>;
+  constexpr int LDS = MODE == 1 ? KV::LDS : MODE == 2 ? QS::LDS : (KV::LDS > QS::LDS ? KV::LDS : QS::LDS);
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int BH = a.B * a.H;
   const int nb = (a.N + 127) / 128;  // 128-row blocks: key blocks of dK/dV, query blocks of dQ
@@ -498,10 +493,10 @@ __global__ __launch_bounds__(kThreads, (grad_occupancy<T, D, MODE>())) void bwd_
   }
   const int rank = i / BH, bh = i % BH;
   if (dkdv) {
-    if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL>(a, rank, bh, lds);  // causal: low key blocks are heaviest
+    if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL, OCC>(a, rank, bh, lds);  // causal: low key blocks are heaviest
   } else {
     if constexpr (MODE != 1)
-      dq_block<T, D, CAUSAL, (grad_occupancy<T, D, MODE>() == 2 && D > 64) ? 1 : DqShape<T, D>::BK / 32>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
+      dq_block<T, D, CAUSAL, (OCC == 2 && D > 64) ? 1 : QS::BK / 32>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
   }
 }
 
@@ -525,12 +520,8 @@ hipError_t launch_one(int stage, const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else if (stage == 3)
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    else if constexpr (fused_grads<T, D>())
+    else
       hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 0>), dim3((unsigned)(2 * grid)), dim3(kThreads), 0, stream, a);
-    else {
-      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 1>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-      hipLaunchKernelGGL((bwd_grad_kernel<T, D, CAUSAL, 2>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    }
   }
   return hipGetLastError();
 }

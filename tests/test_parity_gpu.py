@@ -124,8 +124,9 @@ def check_invariants(inp, got, w):
 @pytest.mark.parametrize("w,nheads_rows,nkeys", [
     (W.GPT2_LONG, 12, 256),
     (W.VERY_LONG, 16, 256),
-    # head dimension 96 at the long-context shape (same recipe and seed)
+    # head dimensions 96 and 128 at the long-context shape (same recipe and seed)
     (dataclasses.replace(W.GPT2_LONG, d=96, name="GPT-2 head long context B=1 H=12 N=8192 d=96 causal, QK x2"), 12, 128),
+    (dataclasses.replace(W.GPT2_LONG, d=128, name="GPT-2 head long context B=1 H=12 N=8192 d=128 causal, QK x2"), 12, 128),
 ])
 def test_long_context_sampled(w, nheads_rows, nkeys):
     """256 random query rows in every head (O, LSE, dQ) and 256 random key rows
@@ -157,7 +158,7 @@ def test_long_context_sampled(w, nheads_rows, nkeys):
     check_invariants(inp, got, w)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 def test_long_ragged_length_sampled(d):
     """A length far past the workloads and off every block size (N = 100003,
     prime), causal: 128 random query rows per head against the oracle, plus the

@@ -1,8 +1,7 @@
 """Compile the gfx950 attention library (libfa.so) in-tree with hipcc.
 
 Every HIP source is built for gfx950 only, with packed-fp32 instruction
-selection disabled and hardware float atomics enabled, then linked into one
-shared library next to this file.
+selection disabled, then linked into one shared library next to this file.
 """
 from __future__ import annotations
 
@@ -23,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -31,6 +31,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                             recomputation page's model and explicit attention)
        python bench.py --compare-explicit  (JSON lines: fwd+bwd time vs explicit attention)
        python bench.py --sweep             (JSON lines: causal H=12 d=64, N = 1k..32k, B = 16384/N)
+       python bench.py --calibrate         (JSON line from the fa_calib microbenchmarks: sustained
+                                            matrix-core rate, exp/FMA rates, matrix/vector overlap,
+                                            LDS and HBM bandwidth, float-atomic rate)
 """
 from __future__ import annotations
 
@@ -294,6 +297,22 @@ def cpu_baseline(w, min_seconds=10.0):
                       f"numpy; {dt:.2f} s for {flops / 1e9:.1f} counted GFLOP"}
 
 
+def calibrate():
+    """Run the fa_calib microbenchmarks (built beside libfa.so) as a child process."""
+    import subprocess
+    exe = os.path.join(ROOT, "io_aware_exact_07_amd", "fa_calib")
+    if not os.path.exists(exe):
+        raise SystemExit(f"{exe} is missing: build it with `python -c \"import __graft_entry__ as g; g.build()\"`")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    line = r.stdout.strip().splitlines()[-1] if r.stdout.strip() else ""
+    if r.returncode != 0 or not line.startswith("{"):
+        raise SystemExit(f"fa_calib failed (exit {r.returncode}): {r.stdout}{r.stderr}")
+    res = json.loads(line)
+    res["mfma_frac_of_peak"] = round(res["mfma_bf16_tflops"] / PEAK_BF16_TFLOPS, 4)
+    res["hbm_frac_of_peak"] = round(res["hbm_copy_tbs"] * 1000.0 / PEAK_HBM_GBS, 4)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +326,8 @@ def main():
                     help="time the tiled path against explicit attention")
     ap.add_argument("--sweep", action="store_true",
                     help="JSON lines: causal H=12 d=64 at N = 1k..32k with B = 16384/N")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run the calibration microbenchmarks (fa_calib) and print their JSON line")
     ap.add_argument("--workload", default="gpt2_long", choices=sorted(WORKLOAD_KEYS),
                     help="which synthetic workload a step runs (default: the long-context GPT-2 head)")
     ap.add_argument("--head-dim", type=int, default=None,
@@ -328,6 +349,9 @@ def main():
         return
     if args.sweep:
         sweep()
+        return
+    if args.calibrate:
+        calibrate()
         return
 
     import torch

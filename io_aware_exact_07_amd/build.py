@@ -2,6 +2,8 @@
 
 Every HIP source is built for gfx950 only, with packed-fp32 instruction
 selection disabled, then linked into one shared library next to this file.
+The calibration microbenchmarks (csrc/fa_calib.hip) become the executable
+fa_calib beside it; `bench.py --calibrate` runs it.
 """
 from __future__ import annotations
 
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
+CALIB = os.path.join(HERE, "fa_calib")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
@@ -39,10 +42,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _calib(verbose: bool) -> str:
+    tmp = CALIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "fa_calib.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on fa_calib.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CALIB)
+    return CALIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        calib = ex.submit(_calib, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        calib.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

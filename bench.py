@@ -222,9 +222,29 @@ def compare_explicit(steps=10):
         torch.cuda.empty_cache()
 
 
+def hbm_model_bytes(B, H, N, d, e, causal):
+    """Per-launch HBM bytes of the forward and the gradient launch: the
+    compulsory count (every input read once, every output written once) and
+    the count of the tiled algorithm with 128-row blocks and no cache, as in
+    the pages' Theorem 2 (each resident block streams every block of the other
+    side that it needs; a causal mask halves the pairs).  The gradient launch
+    streams Q, dO and the two row vectors past each key block (dK/dV list) and
+    K, V past each query block (dQ list)."""
+    heads = B * H
+    nb = -(-N // 128)
+    rereads = (nb * nb / 2 - nb) if causal else (nb * nb - nb)   # block pairs beyond the first read
+    fwd_c = heads * (e * 4 * N * d + 4 * N)                       # q, k, v read, o written; lse
+    grad_c = heads * (e * 4 * N * d + 8 * N + e * 3 * N * d)      # q, k, v, dO, lse2, D in; dk, dv, dq out
+    fwd_t = fwd_c + heads * rereads * (2 * 128 * d * e)
+    grad_t = grad_c + heads * rereads * (2 * 128 * d * e + 2 * 128 * 4 + 2 * 128 * d * e)
+    return {"fwd_compulsory": int(fwd_c), "fwd_tiled_model": int(fwd_t),
+            "grad_compulsory": int(grad_c), "grad_tiled_model": int(grad_t)}
+
+
 def sweep(steps=20, warmup=5):
     """fwd+bwd rate over sequence lengths at a fixed token count: H=12, d=64,
-    causal, N = 1k .. 32k, B = 16384 / N (B = 1 at N = 32k; one JSON line per N)."""
+    causal, N = 1k .. 32k, B = 16384 / N (B = 1 at N = 32k; one JSON line per N,
+    with the compulsory and tiled-model HBM bytes per launch of both kernels)."""
     import torch
     import io_aware_exact_07_amd as fa
     import workloads as W
@@ -252,7 +272,9 @@ def sweep(steps=20, warmup=5):
         f_fwd, f_bwd = w.flops()
         print(json.dumps({"mode": "sweep", "workload": w.name, "B": B, "N": N, "ms_per_step": round(ms, 5),
                           "tflops": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 3),
-                          "pct_peak": round(100 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}),
+                          "pct_peak": round(100 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                          "launches_per_kernel": warmup + steps,
+                          "hbm_model_bytes": hbm_model_bytes(B, 12, N, 64, 2, True)}),
               flush=True)
         del q, k, v, do
         torch.cuda.empty_cache()
@@ -348,7 +370,7 @@ def main():
         compare_explicit()
         return
     if args.sweep:
-        sweep()
+        sweep(steps=min(args.steps, 20), warmup=min(args.warmup, 5))
         return
     if args.calibrate:
         calibrate()

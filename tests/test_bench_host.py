@@ -37,3 +37,29 @@ def test_committed_traffic_records_name_their_kernel_and_commands():
         assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
         kv = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
         assert float(kv["traffic_bytes_per_launch"]) > float(kv["compulsory_bytes_per_launch"]) > 0
+
+
+def test_hbm_model_reproduces_the_committed_traffic_records():
+    """bench.hbm_model_bytes gives the compulsory and tiled-model counts that the
+    committed counter records state for the long-context workload, and the
+    tiled model grows linearly in N at a fixed token count (Theorem 2 with
+    fixed block rows) while the compulsory count stays constant."""
+    import bench
+    m = bench.hbm_model_bytes(1, 12, 8192, 64, 2, True)
+    for kernel, key in (("fwd_kernel", "fwd"), ("bwd_grad_kernel", "grad")):
+        kv = {}
+        with open(bench.traffic_file(kernel)) as f:
+            for line in f:
+                if ":" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        assert int(kv["compulsory_bytes_per_launch"]) == m[f"{key}_compulsory"]
+        assert int(kv["tiled_model_bytes_per_launch"]) == m[f"{key}_tiled_model"]
+    a = bench.hbm_model_bytes(8, 12, 2048, 64, 2, True)
+    b = bench.hbm_model_bytes(4, 12, 4096, 64, 2, True)
+    assert a["fwd_compulsory"] == b["fwd_compulsory"]
+    reread_a = a["fwd_tiled_model"] - a["fwd_compulsory"]
+    reread_b = b["fwd_tiled_model"] - b["fwd_compulsory"]
+    # block pairs beyond the first read, per head (nb^2/2 - nb with nb = N/128),
+    # times heads: 112 * 96 at N = 2048, 480 * 48 at N = 4096
+    assert reread_a * 480 * 48 == reread_b * 112 * 96

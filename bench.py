@@ -280,9 +280,16 @@ def sweep(steps=20, warmup=5):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, min_seconds=10.0):
-    """The oracle as it stands, on whole heads of the workload (as many as fit
-    in about min_seconds, at least one), on this host's cores."""
+def cpu_baseline(w, min_seconds=10.0, max_full_n=8192):
+    """The oracle as it stands, on this host's cores.  Up to N = max_full_n it
+    runs whole heads of the workload (as many as fit in about min_seconds, at
+    least one) through the full forward and backward.  Beyond that one head's
+    score matrix alone is N^2 doubles (8.6 GB at N = 32768), so it runs the
+    oracle's row mode instead: 256 random query rows of one head, each with
+    its own softmax and Jacobian (O, lse and dQ for those rows), and the rate
+    counts the work those rows do: 4 products of 2*n*d flops per row with n
+    allowed keys."""
+    import numpy as np
     import oracle
     import workloads as W
     try:
@@ -292,16 +299,32 @@ def cpu_baseline(w, min_seconds=10.0):
         threads = len(os.sched_getaffinity(0))
     inp = W.make_inputs(w)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = 0
-    t0 = time.perf_counter()
-    for bh in heads:
-        oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.softmax_scale, w.causal, heads=[bh])
-        done += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    f_fwd, f_bwd = w.flops()
-    flops = (f_fwd + f_bwd) * done / len(heads)
+    if w.N <= max_full_n:
+        done = 0
+        t0 = time.perf_counter()
+        for bh in heads:
+            oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.softmax_scale, w.causal, heads=[bh])
+            done += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = time.perf_counter() - t0
+        f_fwd, f_bwd = w.flops()
+        flops = (f_fwd + f_bwd) * done / len(heads)
+        sample = (f"{done} of {len(heads)} heads of the same workload, full forward + backward in float64 "
+                  f"numpy; {dt:.2f} s for {flops / 1e9:.1f} counted GFLOP")
+    else:
+        rows = np.sort(np.random.default_rng(0).choice(w.N, 256, replace=False))
+        b, h = heads[0]
+        L = w.N if inp.get("seqlens") is None else int(inp["seqlens"][b])
+        x = {n: oracle.to_f64(inp[n][b, h]) for n in ("q", "k", "v", "do")}
+        t0 = time.perf_counter()
+        oracle.rows_forward_backward(x["q"], x["k"], x["v"], x["do"], w.softmax_scale, rows, w.causal, L)
+        dt = time.perf_counter() - t0
+        keys = np.minimum(rows + 1, L) if w.causal else np.full(rows.shape, L)
+        flops = float(np.sum(np.where(rows < L, keys, 0))) * 4 * 2 * w.d
+        sample = (f"256 random query rows of one head (O, lse and dQ of those rows, float64 numpy row mode); "
+                  f"{dt:.2f} s for {flops / 1e9:.2f} GFLOP of their products; a whole head would materialise "
+                  f"{w.N}^2 scores")
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -314,9 +337,7 @@ def cpu_baseline(w, min_seconds=10.0):
     except Exception:
         blas = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model, "blas": blas,
-            "sample": f"{done} of {len(heads)} heads of the same workload, full forward + backward in float64 "
-                      f"numpy; {dt:.2f} s for {flops / 1e9:.1f} counted GFLOP"}
+            "cpu_model": cpu_model, "blas": blas, "sample": sample}
 
 
 def calibrate():

@@ -22,7 +22,7 @@ Prints one JSON line.  Besides the whole-step rate it carries:
                 same workload (about 10 s of work), in the same unit
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload gpt2_long|gpt2_small|bert_large|very_long|single_head]
-                       [--head-dim 64|96|128]
+                       [--head-dim 64|96|128] [--cold]
        (the same JSON line for another workload; `traffic` is reported only
         for the default one, whose counters are recorded)
        python bench.py --copy-probe        (plain 256 MiB copy, for counter calibration)
@@ -369,6 +369,9 @@ def main():
                     help="time the tiled path against explicit attention")
     ap.add_argument("--sweep", action="store_true",
                     help="JSON lines: causal H=12 d=64 at N = 1k..32k with B = 16384/N")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each step after writing a 512 MB buffer (L2 and the last-level cache "
+                         "flushed, outside the timed region); reported under cold_cache")
     ap.add_argument("--calibrate", action="store_true",
                     help="run the calibration microbenchmarks (fa_calib) and print their JSON line")
     ap.add_argument("--workload", default="gpt2_long", choices=sorted(WORKLOAD_KEYS),
@@ -460,8 +463,30 @@ def main():
     grads_ms = avg(lambda i: marks[i][1].elapsed_time(marks[i][2]))
     bwd_ms = prep_ms + grads_ms
 
+    cold = None
+    if args.cold:
+        # Each step starts with its inputs out of every cache: a 512 MB write
+        # (twice the last-level cache) runs on the stream before the step's
+        # first event, so it is not timed.
+        flush = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
+        cs = [[mk(), mk(), mk(), mk()] for _ in range(K)]
+        for i in range(K):
+            flush.fill_(i & 0xFF)
+            cs[i][0].record(stream)
+            step(cs[i][1:])
+        torch.cuda.synchronize()
+        med = lambda xs: sorted(xs)[len(xs) // 2]
+        cold = {"ms_per_step": round(med([c[0].elapsed_time(c[3]) for c in cs]), 5),
+                "fwd_ms": round(med([c[0].elapsed_time(c[1]) for c in cs]), 5),
+                "prepare_ms": round(med([c[1].elapsed_time(c[2]) for c in cs]), 5),
+                "dkdv_dq_ms": round(med([c[2].elapsed_time(c[3]) for c in cs]), 5),
+                "flush_bytes": 512 << 20, "statistic": "median of the timed steps"}
+        del flush
+
     f_fwd, f_bwd = w.flops()
     value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    if cold is not None:
+        cold["tflops"] = round((f_fwd + f_bwd) / (cold["ms_per_step"] * 1e-3) / 1e12, 3)
     per_product = f_fwd / 2.0
     launches = {"fwd_kernel": fwd_ms, "bwd_grad_kernel": grads_ms}
     dom = max(launches, key=launches.get)
@@ -491,6 +516,7 @@ def main():
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
         "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv_dq": round(grads_ms, 5)},
+        **({"cold_cache": cold} if cold is not None else {}),
         "effective_tflops": (round(value * float((sl.double() ** 2).sum()) / (B * N * N), 3) if sl is not None
                              else None),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 3),

@@ -12,12 +12,15 @@ Prints one JSON line.  Besides the whole-step rate it carries:
                 gradient kernel that runs the dK/dV and dQ blocks in one
                 launch) against the bf16 dense matrix-core peak: its
                 algorithmic FLOPs (2*N^2*d per matrix product per head, halved
-                when causal, times the products the kernel performs: 2
-                forward, 4 + 3 gradients) over its average
-                duration, timed with HIP events on the stream the kernels run
-                on; `traffic` is the HBM bytes per launch from rocprofv3
-                FETCH_SIZE + WRITE_SIZE counters recorded under profiles/ when
-                they were taken on the current kernel source, else null
+                when causal, times the products the method needs: 2 forward,
+                5 backward -- S, dP, dV, dK, dQ) over its average duration,
+                timed with HIP events on the stream the kernels run on.  The
+                gradient kernel executes 7 products (its dQ blocks recompute S
+                and dP); that rate is reported beside it as
+                `executed_tflops`, never as `achieved`.  `traffic` is the HBM
+                bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE
+                counters recorded under profiles/ when they were taken on the
+                current kernel source, else null
   cpu_baseline  the fp64 CPU oracle timed on this host on whole heads of the
                 same workload (about 10 s of work), in the same unit
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -56,9 +59,11 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD_KEYS = {"single_head": "SINGLE_HEAD_FP32", "gpt2_small": "GPT2_SMALL", "bert_large": "BERT_LARGE_PADDED",
                  "gpt2_long": "GPT2_LONG", "very_long": "VERY_LONG"}
 KERNELS = {
-    # name: (source file, matrix products per score element)
-    "fwd_kernel": ("io_aware_exact_07_amd/csrc/fa_fwd.hip", 2),
-    "bwd_grad_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 7),   # dK/dV (4) and dQ (3) blocks
+    # name: (source file, matrix products per score element the method needs,
+    #        matrix products per score element the kernel executes)
+    "fwd_kernel": ("io_aware_exact_07_amd/csrc/fa_fwd.hip", 2, 2),
+    # backward: S, dP, dV, dK, dQ; the dQ blocks recompute S and dP (4 + 3)
+    "bwd_grad_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 5, 7),
 }
 
 
@@ -105,19 +110,33 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}), flush=True)
 
 
-def explicit_attention_step(q, k, v, do, scale, causal):
+def explicit_mask(B, N, causal, seqlens, device):
+    """Boolean [B or 1, 1, N, N]: key j may be attended by query i (causal
+    and per-sequence key padding; a padded query row has no allowed key)."""
+    import torch
+    allowed = torch.ones(N, N, dtype=torch.bool, device=device)
+    if causal:
+        allowed = allowed.tril()
+    allowed = allowed[None, None]
+    if seqlens is not None:
+        valid = torch.arange(N, device=device)[None, :] < seqlens.to(device=device, dtype=torch.int64)[:, None]
+        allowed = allowed & valid[:, None, :, None] & valid[:, None, None, :]
+    return allowed
+
+
+def explicit_attention_step(q, k, v, do, scale, allowed):
     """Standard attention that materialises the score and probability
     matrices (the baseline the recomputation pages compare against), forward
-    and backward by hand in the input dtype.  Every batched product gets
-    contiguous operands.  Used only to measure memory and time beside the
-    tiled path; returns (o, dq, dk, dv)."""
+    and backward by hand in the input dtype.  `allowed` is explicit_mask();
+    rows with no allowed key (padded queries) get P = 0, so their output and
+    every gradient they feed are 0.  Every batched product gets contiguous
+    operands.  Used only to measure memory and time beside the tiled path;
+    returns (o, dq, dk, dv)."""
     import torch
-    N = q.shape[2]
     kt = k.transpose(-1, -2).contiguous()
     s = torch.matmul(q, kt).float() * scale
-    if causal:
-        s.masked_fill_(torch.ones(N, N, dtype=torch.bool, device=q.device).triu_(1), float("-inf"))
-    p = torch.softmax(s, dim=-1).to(q.dtype)
+    s.masked_fill_(~allowed, float("-inf"))
+    p = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0).to(q.dtype)
     del s
     o = torch.matmul(p, v)
     pt = p.transpose(-1, -2).contiguous()
@@ -173,7 +192,7 @@ def memory_scaling(seq_lens=(512, 2048, 8192, 32768), layers=12, d_model=768, he
             torch.cuda.synchronize()
             torch.cuda.reset_peak_memory_stats()
             b0 = torch.cuda.memory_allocated()
-            r = explicit_attention_step(q, k, v, do, 1.0 / d ** 0.5, True)
+            r = explicit_attention_step(q, k, v, do, 1.0 / d ** 0.5, explicit_mask(1, N, True, None, dev))
             torch.cuda.synchronize()
             rec["explicit_one_layer_peak_extra_bytes"] = torch.cuda.max_memory_allocated() - b0
             del r, q, k, v, do
@@ -198,14 +217,13 @@ def compare_explicit(steps=10):
             o, lse = fa.forward(q, k, v, causal=w.causal, seqlens=sl)
             fa.backward(q, k, v, o, do, lse, causal=w.causal, seqlens=sl)
 
+        allowed = explicit_mask(w.B, w.N, w.causal, sl, dev)   # built once, outside the timed region
+
         def explicit():
-            explicit_attention_step(q, k, v, do, w.softmax_scale, w.causal)
+            explicit_attention_step(q, k, v, do, w.softmax_scale, allowed)
 
         res = {"mode": "compare_explicit", "workload": w.name}
-        for name, fn in (("tiled", ours), ("explicit", explicit if sl is None else None)):
-            if fn is None:
-                res[name + "_ms"] = None   # explicit baseline has no key-padding mask
-                continue
+        for name, fn in (("tiled", ours), ("explicit", explicit)):
             fn()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -215,8 +233,7 @@ def compare_explicit(steps=10):
             b.record()
             torch.cuda.synchronize()
             res[name + "_ms"] = round(a.elapsed_time(b) / steps, 4)
-        if res.get("explicit_ms"):
-            res["speedup"] = round(res["explicit_ms"] / res["tiled_ms"], 2)
+        res["speedup"] = round(res["explicit_ms"] / res["tiled_ms"], 2)
         print(json.dumps(res), flush=True)
         del q, k, v, do
         torch.cuda.empty_cache()
@@ -491,6 +508,7 @@ def main():
     launches = {"fwd_kernel": fwd_ms, "bwd_grad_kernel": grads_ms}
     dom = max(launches, key=launches.get)
     achieved = KERNELS[dom][1] * per_product / (launches[dom] * 1e-3) / 1e12
+    executed = KERNELS[dom][2] * per_product / (launches[dom] * 1e-3) / 1e12
     e = 2 if w.dtype == "bf16" else 4
     compulsory = e * 4 * B * H * N * d + 4 * B * H * N                 # forward: q, k, v, o + lse
     compulsory += e * 2 * B * H * N * d + 4 * B * H * N                # prepare: o, dO -> D
@@ -530,6 +548,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
+            "algorithmic_gflop_per_launch": round(KERNELS[dom][1] * per_product / 1e9, 3),
+            "executed_tflops": round(executed, 3),
+            "executed_products_per_score": KERNELS[dom][2],
             "traffic": traffic,
             "traffic_gbs": None if traffic is None else round(traffic / (launches[dom] * 1e-3) / 1e9, 1),
             "avg_launch_ms": round(launches[dom], 5),

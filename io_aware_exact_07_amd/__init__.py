@@ -109,6 +109,12 @@ def fa_status_string(status: int) -> str:
 
 
 # ---- torch helpers ----------------------------------------------------------
+#
+# Every argument is checked here before any pointer reaches the library: a
+# host, wrongly typed or short lse / workspace / gradient tensor would
+# otherwise make the kernels read or write out of bounds.  The checks compare
+# each tensor with q (shape, dtype, device, contiguity) and only at the end
+# require q to live on a GPU, so each one is testable on a host without one.
 
 def _torch():
     import torch
@@ -124,45 +130,82 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check(ts, shape, dev, dt):
+def _check(ts, shape, dev, dt, what="q, k, v, o, do, dq, dk, dv"):
     for t in ts:
         if t.shape != shape or t.device != dev or t.dtype != dt or not t.is_contiguous():
-            raise ValueError("q, k, v, o, do, dq, dk, dv must be contiguous [B,H,N,d] tensors of one dtype "
-                             "on one device")
+            raise ValueError(f"{what} must be contiguous [B,H,N,d] tensors of one dtype on one device")
+
+
+def _check_lse(lse, q):
+    torch = _torch()
+    B, H, N, _ = q.shape
+    if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 [B,H,N] = [{B},{H},{N}] tensor on {q.device}, "
+                         f"got {tuple(lse.shape)} {lse.dtype} on {lse.device}")
+
+
+def _check_workspace(ws, q, need):
+    nbytes = ws.numel() * ws.element_size()
+    if ws.device != q.device or not ws.is_contiguous() or nbytes < need:
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on {q.device}, "
+                         f"got {nbytes} bytes on {ws.device}")
+
+
+def _on_gpu(q):
+    if q.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU (got {q.device}): the library takes device pointers")
 
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream, dev):
+def _stream_ctx(stream):
+    """Context that makes `stream` current, so that every tensor allocated
+    for a call (outputs, workspace, the seqlens copy) belongs to the stream the
+    kernels run on: the caching allocator then never hands that memory to
+    other work before the kernels are done, and the seqlens copy is ordered
+    before them."""
     torch = _torch()
-    s = torch.cuda.current_stream(dev) if stream is None else stream
-    return s.cuda_stream
+    import contextlib
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
-def _seqlens(seqlens, dev, B):
+def _check_seqlens(seqlens, B):
+    if seqlens is not None and tuple(seqlens.shape) != (B,):
+        raise ValueError(f"seqlens must have shape [B] = [{B}], got {tuple(seqlens.shape)}")
+
+
+def _seqlens(seqlens, dev):
     torch = _torch()
     if seqlens is None:
         return None
-    s = seqlens.to(device=dev, dtype=torch.int32).contiguous()
-    if s.shape != (B,):
-        raise ValueError("seqlens must have shape [B]")
-    return s
+    return seqlens.to(device=dev, dtype=torch.int32).contiguous()
 
 
 def forward(q, k, v, causal=False, scale=None, seqlens=None, out=None, lse=None, stream=None):
-    """o, lse = attention forward.  q, k, v: [B,H,N,d] bf16 or fp32 on the GPU."""
+    """o, lse = attention forward.  q, k, v: [B,H,N,d] bf16 or fp32 on the GPU.
+
+    With `stream` the outputs are allocated and the kernels run on that
+    stream (the caller orders q, k, v before it)."""
     torch = _torch()
     B, H, N, d = q.shape
     _check((q, k, v), q.shape, q.device, q.dtype)
+    if out is not None:
+        _check((out,), q.shape, q.device, q.dtype, "out")
+    if lse is not None:
+        _check_lse(lse, q)
+    _check_seqlens(seqlens, B)
+    code = _dtype_code(q)
+    _on_gpu(q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
-    _check((o,), q.shape, q.device, q.dtype)
-    sl = _seqlens(seqlens, q.device, B)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, H, N, d, scale,
-                causal, _ptr(sl), _dtype_code(q), _stream(stream, q.device))
+    with _stream_ctx(stream):
+        o = torch.empty_like(q) if out is None else out
+        lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+        sl = _seqlens(seqlens, q.device)
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, H, N, d, scale,
+                    causal, _ptr(sl), code, torch.cuda.current_stream(q.device).cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd")
     return o, lse_t
@@ -170,23 +213,37 @@ def forward(q, k, v, causal=False, scale=None, seqlens=None, out=None, lse=None,
 
 def backward(q, k, v, o, do, lse, causal=False, scale=None, seqlens=None, workspace=None, grads=None,
              stream=None):
-    """dq, dk, dv = attention backward, recomputing every score block."""
+    """dq, dk, dv = attention backward, recomputing every score block.
+
+    `workspace` (optional) is any contiguous tensor on q's device of at least
+    fa_bwd_workspace_bytes() bytes.  With `stream` the gradients and the
+    workspace are allocated and the kernels run on that stream."""
     torch = _torch()
     B, H, N, d = q.shape
     _check((q, k, v, o, do), q.shape, q.device, q.dtype)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check_lse(lse, q)
     code = _dtype_code(q)
     need = fa_bwd_workspace_bytes(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = grads
-    _check((dq, dk, dv), q.shape, q.device, q.dtype)
-    sl = _seqlens(seqlens, q.device, B)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, causal, _ptr(sl),
-                workspace.data_ptr(), workspace.numel(), code, _stream(stream, q.device))
+    if workspace is not None:
+        _check_workspace(workspace, q, need)
+    if grads is not None:
+        if len(grads) != 3:
+            raise ValueError("grads must be (dq, dk, dv)")
+        _check(grads, q.shape, q.device, q.dtype, "dq, dk, dv")
+    _check_seqlens(seqlens, B)
+    _on_gpu(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with _stream_ctx(stream):
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+        if grads is None:
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        dq, dk, dv = grads
+        sl = _seqlens(seqlens, q.device)
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale, causal, _ptr(sl),
+                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), code,
+                    torch.cuda.current_stream(q.device).cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv

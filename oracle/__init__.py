@@ -13,8 +13,10 @@ Contents
 
 Parity status: every function here is pinned by tests/test_oracle.py
 (closed forms, invariants, finite differences, mpmath, an independent
-library routine) or tests/test_memory_model.py (values printed on the page).
-Nothing here is "parity unpinned".
+library routine -- the batched wrappers head by head against torch's float64
+scaled-dot-product attention with per-sequence lengths) or
+tests/test_memory_model.py (values printed on the page).  Nothing here is
+"parity unpinned".
 """
 from .attention import (allowed_mask, head_forward, head_backward, attention_forward, attention_backward,
                         rows_forward_backward, key_columns_backward, to_f64)

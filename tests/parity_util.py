@@ -49,3 +49,28 @@ def lse_err(got, ref):
 
 def valid_rows(seqlens, b, N):
     return N if seqlens is None else int(min(max(int(seqlens[b]), 0), N))
+
+
+def host_workers(per_job_bytes, cap=16):
+    """Thread count for oracle jobs: at most the host's CPUs (16 on a one-GPU
+    box) and as many jobs as fit in half the free memory (64 GB at most)."""
+    import os
+    try:
+        import psutil
+        free = psutil.virtual_memory().available
+    except Exception:
+        free = 32 << 30
+    budget = min(64 << 30, free // 2)
+    n = min(cap, len(os.sched_getaffinity(0)), max(1, int(budget // max(per_job_bytes, 1))))
+    return max(1, n)
+
+
+def parallel_map(fn, jobs, workers):
+    """[fn(j) for j in jobs] on a thread pool, BLAS held to one thread per call
+    so the workers do not oversubscribe the cores (numpy's array kernels and
+    BLAS release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, jobs))

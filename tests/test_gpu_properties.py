@@ -181,3 +181,52 @@ def test_stored_activations_equal_the_recomputation_page_model():
         model = training_memory(N, d_model=768, heads=12, layers=12, elem_bytes=2)
         assert stored + inputs == round(model.recompute_gb * 1e9)
         del outs, qkv
+
+
+def test_side_stream_matches_default_stream_bitwise():
+    """forward/backward with stream= run, allocate and copy seqlens on that
+    stream; the results equal the default-stream run bit for bit."""
+    inp = W.random_inputs(3, 2, 333, 64, "bf16", seed=44, gain=1.5, seqlens=[333, 100, 7])
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    sl = inp["seqlens"]                      # host tensor: the binding copies it on the call's stream
+    ref_o, ref_l = fa.forward(q, k, v, causal=True, seqlens=sl)
+    ref_g = fa.backward(q, k, v, ref_o, do, ref_l, causal=True, seqlens=sl)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, lse = fa.forward(q, k, v, causal=True, seqlens=sl, stream=side)
+    g = fa.backward(q, k, v, o, do, lse, causal=True, seqlens=sl, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal,seqlens", [(True, None), (False, [200, 77, 1])])
+def test_explicit_baseline_matches_the_oracle(causal, seqlens):
+    """The explicit-attention baseline that bench.py --compare-explicit times
+    (materialised P, hand-written backward, causal or key-padding mask)
+    computes the same attention as the oracle within the bf16 tolerances, with
+    zero outputs and gradients at padded positions."""
+    import numpy as np
+    import oracle
+    from bench import explicit_attention_step, explicit_mask
+    from parity_util import TOL, f64, lse_err, rel_err
+    B = 2 if seqlens is None else len(seqlens)
+    H, N, d = 2, 200, 64
+    inp = W.random_inputs(B, H, N, d, "bf16", seed=8, gain=1.5, seqlens=seqlens)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    sl = None if inp["seqlens"] is None else inp["seqlens"].to(DEV)
+    allowed = explicit_mask(B, N, causal, sl, DEV)
+    got = [t.cpu() for t in explicit_attention_step(q, k, v, do, 0.125, allowed)]
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], 0.125, causal,
+                                    None if seqlens is None else np.array(seqlens))
+    tol = TOL["bf16"]
+    for b in range(B):
+        L = N if seqlens is None else seqlens[b]
+        for h in range(H):
+            for name, t in zip(("o", "dq", "dk", "dv"), got):
+                g = f64(t[b, h])
+                assert rel_err(g[:L], ref[name][b, h][:L]) <= tol[name], (name, b, h)
+                assert np.all(g[L:] == 0), (name, b, h)

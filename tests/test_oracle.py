@@ -223,6 +223,68 @@ def test_batched_wrappers_follow_seqlens():
                 assert np.array_equal(r[n][b, h], one[n])
 
 
+def _check_batched_forward(fwd, x, seq, causal, scale):
+    """Every head of a batched forward against torch's CPU float64
+    scaled_dot_product_attention (an independent library routine) with the
+    per-sequence mask, and LSE against torch.logsumexp of the masked scores.
+    Returns True if every head matches."""
+    B, H, N, d = x[0].shape
+    O, LSE = fwd(*x[:3], scale=scale, causal=causal, seqlens=seq)
+    for b in range(B):
+        L = int(seq[b])
+        for h in range(H):
+            if not (np.all(O[b, h, L:] == 0) and np.all(np.isneginf(LSE[b, h, L:]))):
+                return False
+            if L == 0:
+                continue
+            q, k, v = (t[b, h].double() for t in x[:3])
+            mask = torch.tensor(oracle.allowed_mask(N, L, causal)[:L])
+            o = torch.nn.functional.scaled_dot_product_attention(q[None, None, :L], k[None, None], v[None, None],
+                                                                 attn_mask=mask, scale=scale)[0, 0]
+            s = (q[:L] @ k.T * scale).masked_fill(~mask, float("-inf"))
+            lse = torch.logsumexp(s, dim=1)
+            if not (np.allclose(O[b, h, :L], o.numpy(), atol=1e-12, rtol=0)
+                    and np.allclose(LSE[b, h, :L], lse.numpy(), atol=1e-12, rtol=0)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_batched_forward_matches_library_routine_per_head(causal):
+    """attention_forward over [B, H, N, d] with per-sequence lengths: each head
+    uses its own sequence's length (B != H, lengths 12, 5, 1 and 0)."""
+    B, H, N, d = 4, 3, 12, 4
+    x = [torch.tensor(rnd((B, H, N, d), 10 + s, 1.5)) for s in range(3)]
+    seq = np.array([12, 5, 1, 0])
+    assert _check_batched_forward(oracle.attention_forward, x, seq, causal, 0.45)
+    # the heads argument computes only the listed heads and leaves the rest NaN
+    O, LSE = oracle.attention_forward(*x, scale=0.45, causal=causal, seqlens=seq, heads=[(1, 2)])
+    full_o, full_lse = oracle.attention_forward(*x, scale=0.45, causal=causal, seqlens=seq)
+    assert np.array_equal(O[1, 2], full_o[1, 2]) and np.array_equal(LSE[1, 2], full_lse[1, 2])
+    assert np.isnan(O[0, 0]).all() and np.isnan(LSE[3, 1]).all()
+
+
+def test_batched_forward_pin_catches_a_head_indexed_length():
+    """A plausible slip in the batched wrapper, taking the length of sequence h
+    instead of sequence b, fails the pin above."""
+    def mutant(q, k, v, scale, causal=False, seqlens=None, heads=None):
+        q, k, v = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+        B, H, N, d = q.shape
+        O = np.full((B, H, N, d), np.nan)
+        LSE = np.full((B, H, N), np.nan)
+        for b in range(B):
+            for h in range(H):
+                L = int(min(max(int(seqlens[h]), 0), N))
+                o, lse, _ = oracle.head_forward(q[b, h], k[b, h], v[b, h], scale, causal, L)
+                O[b, h], LSE[b, h] = o, lse
+        return O, LSE
+    B, H, N, d = 4, 3, 12, 4
+    x = [torch.tensor(rnd((B, H, N, d), 10 + s, 1.5)) for s in range(3)]
+    seq = np.array([12, 5, 1, 0])
+    for causal in (False, True):
+        assert not _check_batched_forward(mutant, x, seq, causal, 0.45)
+
+
 # ---------------------------------------------------------------------------
 # Planted mistakes: each mutant of the oracle must be caught by a pin above.
 

@@ -29,8 +29,10 @@
  * Ownership: the caller allocates and frees every buffer, including the
  * backward workspace; the library never allocates or frees device memory and
  * keeps no pointer after a call returns (kernels already queued on `stream`
- * still read and write the buffers until they finish).  The library holds
- * no mutable global state, so calls from several threads are safe.
+ * still read and write the buffers until they finish).  The only mutable
+ * global state is fa_bwd_noalloc's per-device scratch array and its address
+ * table (guarded by a mutex); every other entry point is stateless, so calls
+ * from several threads are safe.
  *
  * Ordering: every call only enqueues work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns; the caller synchronises.
@@ -60,8 +62,12 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scale or dtype */
   FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64, 96 or 128 */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_bytes() */
-  FA_ERR_HIP = -4          /* a kernel launch failed */
+  FA_ERR_HIP = -4,         /* a kernel launch failed */
+  FA_ERR_SCRATCH = -5      /* fa_bwd_noalloc: row vectors exceed FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
+
+/* Size of fa_bwd_noalloc's static device scratch array, per GPU. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32).
@@ -97,6 +103,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal,
            const int32_t* seqlens, void* workspace, size_t workspace_bytes,
            int dtype, void* stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and results (bit for bit)
+ * as fa_bwd; the row vectors live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
+ * until the process ends.  Its address on the current device is looked up
+ * with hipGetSymbolAddress on the first call on that device.  The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating library routine).
+ * Limit: fa_bwd_workspace_bytes(B, H, N, d, dtype) must not exceed
+ * FA_NOALLOC_SCRATCH_BYTES (B*H*ceil(N/128)*128 <= 2^21 rows), else
+ * FA_ERR_SCRATCH is returned before any HIP call.  Nothing in the array needs
+ * clearing: each call rewrites every row it reads.  Every call on a GPU shares
+ * that GPU's array, so calls whose work overlaps on one GPU (several streams
+ * or host threads without ordering between them) race: order them.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* seqlens, int dtype, void* stream);
 
 /*
  * The stages of fa_bwd, exposed for callers that time them separately or

@@ -6,7 +6,7 @@ PyTorch supplies device memory and the stream.  If the library has not been
 built the import of the native part fails loudly; there is no fallback.
 
 Raw entry points (same names and argument order as the C ABI, pointers as
-ints): fa_fwd, fa_bwd, fa_bwd_prepare, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dkdv_dq,
+ints): fa_fwd, fa_bwd, fa_bwd_noalloc, fa_bwd_prepare, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dkdv_dq,
 fa_bwd_workspace_bytes, fa_status_string.
 Tensor helpers: forward(q, k, v, ...) -> (o, lse) and
 backward(q, k, v, o, do, lse, ...) -> (dq, dk, dv).
@@ -27,6 +27,8 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
+FA_ERR_SCRATCH = -5
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -52,6 +54,8 @@ def lib():
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
         L.fa_bwd.restype = ci
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, ci, vp]
+        L.fa_bwd_noalloc.restype = ci
         L.fa_bwd_prepare.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, vp, sz, ci, vp]
         L.fa_bwd_prepare.restype = ci
         L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp, vp, sz, ci, vp]
@@ -76,6 +80,11 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, 
            dtype, stream) -> int:
     return lib().fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, int(bool(causal)), seqlens,
                         workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, seqlens, dtype, stream) -> int:
+    return lib().fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, int(bool(causal)), seqlens,
+                                dtype, stream)
 
 
 def fa_bwd_prepare(o, dO, lse, B, H, N, d, seqlens, workspace, workspace_bytes, dtype, stream) -> int:

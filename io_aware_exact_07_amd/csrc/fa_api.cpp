@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "fa_launch.h"
 
 namespace {
@@ -58,10 +60,12 @@ namespace {
 
 enum Stage { kAll = 0, kPrepare = 1, kDkDv = 2, kDq = 3, kGrads = 4 };
 
-// Shared validation of the backward entry points; fills `a` on success.
-int bwd_setup(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens,
-              void* workspace, size_t workspace_bytes, int dtype, int stage, fa::BwdArgs* a) {
+// Validation of the backward entry points' shapes, scalars and tensor
+// pointers (everything but the workspace).  Returns FA_OK, an error, or 1
+// for "empty: nothing to do".
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+              void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens, int dtype,
+              int stage) {
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
   const bool compute = stage == kAll || stage == kDkDv || stage == kDq || stage == kGrads;
@@ -74,6 +78,15 @@ int bwd_setup(const void* q, const void* k, const void* v, const void* o, const 
   if ((stage == kAll || stage == kDq || stage == kGrads) && !tensor_ok(dq)) return FA_ERR_INVALID_ARG;
   if (compute && (lse == nullptr || !aligned(lse, 4))) return FA_ERR_INVALID_ARG;
   if (seqlens != nullptr && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// bwd_check plus the workspace; fills `a` on success.
+int bwd_setup(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, const int32_t* seqlens,
+              void* workspace, size_t workspace_bytes, int dtype, int stage, fa::BwdArgs* a) {
+  int st = bwd_check(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, stage);
+  if (st != FA_OK) return st;
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
   if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need) return FA_ERR_WORKSPACE;
   float* lse2 = static_cast<float*>(workspace);
@@ -118,6 +131,67 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                      kAll, &a);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
+  st = run_stage(kPrepare, a, d, dtype, causal, stream);
+  if (st != FA_OK) return st;
+  return run_grads(a, d, dtype, causal, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace is a static device array.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory, so the
+// kernels only ever receive the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept here.
+namespace {
+
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, or nullptr on a HIP error.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* seqlens, int dtype, void* stream) {
+  // Every argument is validated, and problems whose row vectors exceed the
+  // array are rejected, before any HIP call.
+  int st = bwd_check(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, dtype, kAll);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (fa_bwd_workspace_bytes(B, H, N, d, dtype) > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return FA_ERR_HIP;
+  fa::BwdArgs a;
+  st = bwd_setup(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, seqlens, ws, kScratchBytes, dtype, kAll, &a);
+  if (st != FA_OK) return st;
+  // The row vectors are fully rewritten by the prepare stage (padding rows
+  // included), so nothing in the array needs clearing between calls.
   st = run_stage(kPrepare, a, d, dtype, causal, stream);
   if (st != FA_OK) return st;
   return run_grads(a, d, dtype, causal, stream);
@@ -173,6 +247,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64, 96 or 128)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "problem too large for the allocation-free entry point's static scratch (see FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -100,6 +100,27 @@ def test_stage_validation():
                              fa.FA_BF16, None) == fa.FA_ERR_WORKSPACE
 
 
+def test_noalloc_validation_and_size_limit():
+    """The allocation-free backward validates like fa_bwd and rejects problems
+    whose row vectors exceed its static array before any HIP call."""
+    def na(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dO=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=1, N=128, d=64,
+                 scale=0.125, causal=0, seqlens=None, dtype=fa.FA_BF16, stream=None)
+        a.update(kw)
+        return fa.fa_bwd_noalloc(*a.values())
+    assert na(dq=None) == fa.FA_ERR_INVALID_ARG
+    assert na(lse=FAKE + 2) == fa.FA_ERR_INVALID_ARG
+    assert na(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert na(B=0) == fa.FA_OK
+    limit = fa.FA_NOALLOC_SCRATCH_BYTES
+    # 2^21 padded rows fill the array exactly; one more 128-row block does not fit
+    assert fa.fa_bwd_workspace_bytes(1, 16, 1 << 17, 64, fa.FA_BF16) == limit
+    assert fa.fa_bwd_workspace_bytes(1, 16, (1 << 17) + 1, 64, fa.FA_BF16) > limit
+    assert na(H=16, N=(1 << 17) + 1) == fa.FA_ERR_SCRATCH
+    assert na(B=64, H=64, N=1024) == fa.FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_status_string(fa.FA_ERR_SCRATCH)
+
+
 def test_workspace_is_linear_in_N_and_holds_row_vectors():
     for dt in (fa.FA_BF16, fa.FA_FP32):
         for d in (64, 96, 128):
@@ -113,6 +134,7 @@ def test_workspace_is_linear_in_N_and_holds_row_vectors():
 
 
 def test_status_strings():
-    for s in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_WORKSPACE, fa.FA_ERR_HIP):
+    for s in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_WORKSPACE, fa.FA_ERR_HIP,
+              fa.FA_ERR_SCRATCH):
         assert fa.fa_status_string(s) and fa.fa_status_string(s) != "unknown status"
     assert fa.fa_status_string(12345) == "unknown status"

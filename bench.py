@@ -69,7 +69,7 @@ KERNELS = {
 
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNELS[kernel][0], "io_aware_exact_07_amd/csrc/fa_common.h"):
+    for rel in (KERNELS[kernel][0], "io_aware_exact_07_amd/csrc/fa_common.h", "io_aware_exact_07_amd/csrc/fa_place.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -26,6 +26,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_place.h"
 
 namespace fa {
 
@@ -484,19 +485,30 @@ __global__ __launch_bounds__(kThreads, (grad_occupancy<T, D, MODE>())) void bwd_
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int BH = a.B * a.H;
   const int nb = (a.N + 127) / 128;  // 128-row blocks: key blocks of dK/dV, query blocks of dQ
-  int i = blockIdx.x;
+  // Work item of this workgroup: a head and a block level, heaviest level
+  // first (causal: low key blocks, high query blocks).  A single-list launch
+  // keeps each head's blocks on as few XCDs as the balance allows, so the
+  // tiles they all stream (Q and dO for dK/dV, K and V for dQ) are read into
+  // one L2.  MODE 0 interleaves the lists rank by rank over all heads
+  // instead: there the dK/dV and dQ blocks of a head stream different
+  // tensors, so placing them together shares nothing, and this order spreads
+  // each XCD's lists over the fewest heads of either kind (measured: fewer
+  // bytes and a shorter launch on the long-context workload).
+  int bh, level;
   bool dkdv = MODE == 1;
   if (MODE == 0) {
+    const int i = blockIdx.x;
     const int r = i / (2 * BH), j = i % (2 * BH);
     dkdv = j < BH;
-    i = r * BH + (dkdv ? j : j - BH);
-  }
-  const int rank = i / BH, bh = i % BH;
-  if (dkdv) {
-    if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL, OCC>(a, rank, bh, lds);  // causal: low key blocks are heaviest
+    bh = dkdv ? j : j - BH;
+    level = nb - 1 - r;
   } else {
-    if constexpr (MODE != 1)
-      dq_block<T, D, CAUSAL, (OCC == 2 && D > 64) ? 1 : QS::BK / 32>(a, CAUSAL ? nb - 1 - rank : rank, bh, lds);
+    place_workgroup(make_placement(BH, nb), blockIdx.x, 0, bh, level);
+  }
+  if (dkdv) {
+    if constexpr (MODE != 2) dkdv_block<T, D, CAUSAL, OCC>(a, nb - 1 - level, bh, lds);
+  } else {
+    if constexpr (MODE != 1) dq_block<T, D, CAUSAL, (OCC == 2 && D > 64) ? 1 : QS::BK / 32>(a, level, bh, lds);
   }
 }
 

@@ -26,6 +26,7 @@
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_place.h"
 
 namespace fa {
 
@@ -35,7 +36,7 @@ constexpr int kFwdBQ = 128;
 constexpr int kFwdBK = 64;
 constexpr int kFwdThreads = 256;
 constexpr float kSlack = 8.0f;  // probabilities are formed relative to a max at most 2^8 stale
-constexpr int kCUs = 256;        // compute units of an MI355X: the dispatch stride that shares a CU
+constexpr int kCUs = 256;        // compute units of an MI355X: workgroups g and g + kCUs share a CU
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(FwdArgs a) {
@@ -69,18 +70,14 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int BH = a.B * a.H;
   const int nqb = (a.N + BQ - 1) / BQ;
-  // Causal: block work grows with the query block index.  Workgroups are
-  // dispatched in index order across the CUs, so indices i, i + kCUs,
-  // i + 2 kCUs, ... tend to share a CU.  Ranking blocks heaviest first and
-  // reversing every other group of kCUs pairs heavy with light blocks on a CU.
-  int idx = blockIdx.x;
-  if (CAUSAL) {
-    const int g = idx / kCUs, t = idx % kCUs;
-    const int total = (int)gridDim.x;
-    if ((g & 1) && (g + 1) * kCUs <= total) idx = g * kCUs + (kCUs - 1 - t);
-  }
-  const int qb = CAUSAL ? (nqb - 1 - idx / BH) : idx / BH;
-  const int bh = idx % BH;
+  // Which query block of which head this workgroup takes: heads stay on as
+  // few XCDs as the balance allows, so their K/V tiles are shared in one L2,
+  // and each XCD runs its blocks heaviest first (causal work grows with the
+  // query block index).  Workgroups g and g + kCUs share a compute unit, so
+  // under the causal mask every other group of kCUs is reversed to pair heavy
+  // with light blocks there.
+  int bh, qb;
+  place_workgroup(make_placement(BH, nqb), blockIdx.x, CAUSAL ? kCUs / 8 : 0, bh, qb);
   const int b = bh / a.H;
   const int L = clamp_len(a.seqlens, b, a.N);
   const size_t hoff = (size_t)bh * a.N * D;

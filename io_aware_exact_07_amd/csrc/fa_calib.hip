@@ -8,8 +8,19 @@
 //   mix       one wave alternating one product with four exponentials (no data
 //             dependence between them): how far the matrix core and the vector
 //             ALU overlap inside a wave
-//   split     the same work with even waves doing only products and odd waves
-//             only exponentials: how far they overlap across waves
+//   split     the same work in 8-wave groups, waves 0-3 doing only products and
+//             waves 4-7 only exponentials; waves w and w+4 share SIMD w, so
+//             this is how far two waves of one SIMD overlap the two pipes
+//   lds_frag  the attention kernels' LDS fragment reads on a swizzled
+//             128 x 64 bf16 tile, 2 four-wave groups per CU: row fragments
+//             (ds_read_b128) and transposed column fragments
+//             (ds_read_b64_tr_b16), bytes per ns per CU
+//   mfma_lds  8-wave groups, waves 0-3 products, waves 4-7 conflict-free
+//             ds_read_b128 reads: whether LDS reads slow the products of
+//             another wave on the same SIMD
+//   placement where a 1536-group launch lands: XCD of group g (hardware
+//             register) against g % 8, and whether g and g + 256 share a
+//             compute unit
 //   lds       ds_read_b128 from conflict-free addresses: LDS read bandwidth
 //   copy      1 GiB device-to-device copy: HBM bandwidth (read + write bytes)
 //   atomic    device-scope float atomic adds spread over 32 MiB: the rate a
@@ -19,7 +30,10 @@
 // against the grid before launch) and every loop has a fixed trip count.
 #include <hip/hip_runtime.h>
 
+#include "fa_common.h"
+
 #include <algorithm>
+#include <utility>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -99,12 +113,12 @@ __global__ __launch_bounds__(kThreads) void k_valu(float* out, int iters, float 
 // iteration).  MODE 1: even waves 16 products, odd waves 64 exponentials per
 // iteration (the same total work per pair of waves).
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_overlap(float* out, int iters, float seed) {
+__global__ __launch_bounds__(2 * kThreads) void k_overlap(float* out, int iters, float seed) {
   const bf16x8 a = frag(seed), b = frag(seed * 0.5f);
   f32x16 c0 = {}, c1 = {};
   float e0 = -seed, e1 = -2 * seed, e2 = -3 * seed, e3 = -4 * seed, e4 = -5 * seed, e5 = -6 * seed,
         e6 = -7 * seed, e7 = -8 * seed;
-  const bool odd = (threadIdx.x >> 6) & 1;
+  const bool odd = MODE == 1 ? (threadIdx.x >> 6) >= 4 : false;  // MODE 1: 8-wave groups, waves 4-7
   for (int it = 0; it < iters; ++it) {
     if (MODE == 0) {
 #pragma unroll
@@ -124,10 +138,8 @@ __global__ __launch_bounds__(kThreads) void k_overlap(float* out, int iters, flo
   }
   // The products' results are read only after these wait states.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
-  out[blockIdx.x * kThreads + threadIdx.x] = e0 + e1 + e2 + e3 + e4 + e5 + e6 + e7 + sum16(c0) + sum16(c1);
+  out[blockIdx.x * blockDim.x + threadIdx.x] = e0 + e1 + e2 + e3 + e4 + e5 + e6 + e7 + sum16(c0) + sum16(c1);
 }
-#undef MF
-#undef EX
 
 // 8 ds_read_b128 per iteration per lane from a 64 KiB buffer; lanes read
 // consecutive 16-byte chunks, so every read is conflict-free.
@@ -147,6 +159,84 @@ __global__ __launch_bounds__(kThreads) void k_lds(unsigned* out, int iters) {
     }
   }
   out[blockIdx.x * kThreads + threadIdx.x] = acc.x + acc.y + acc.z + acc.w;
+}
+
+// LDS fragment reads as the attention kernels issue them: a swizzled
+// 128 x 64 bf16 tile (fa::Tile), ROW = 8 row fragments (ds_read_b128) or
+// COL = 16 transposed reads (ds_read_b64_tr_b16) per iteration, every address
+// a fa::FragAddr offset inside the tile.
+template <bool ROW>
+__global__ __launch_bounds__(kThreads, 2) void k_lds_frag(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) fa::bf16 tile[2 * 128 * 64];
+  for (int i = threadIdx.x; i < 2 * 128 * 64; i += kThreads) tile[i] = (fa::bf16)(float)((i * 7) % 13);
+  __syncthreads();
+  fa::FragAddr<fa::bf16, 64> fr;
+  fr.init(threadIdx.x & 63);
+  float acc = 0.f;
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" ::: "memory");  // keep the reads inside the loop
+    fa::bf16x8 x = {};
+    const int q = it & 3;
+    if (ROW) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) { x += fr.row(tile, q, c); x += fr.row(tile + 128 * 64, q, c); }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) { x += fr.col(tile, 32 * q + 16 * cc, t); x += fr.col(tile + 128 * 64, 32 * q + 16 * cc, t); }
+    }
+    acc += (float)x[0] + (float)x[7];
+  }
+  out[blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+// 8-wave groups: waves 0-3 issue independent products (MODE 0 and 1), waves
+// 4-7 conflict-free ds_read_b128 (MODE 1 and 2).
+template <int MODE>
+__global__ __launch_bounds__(2 * kThreads) void k_mfma_lds(float* out, int iters, float seed) {
+  __shared__ uint4 buf[1024];
+  for (int i = threadIdx.x; i < 1024; i += 2 * kThreads) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float r = 0.f;
+  if (w < 4 && MODE != 2) {
+    const bf16x8 a = frag(seed), b = frag(seed * 0.5f);
+    f32x16 c0 = {}, c1 = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { MF(c0); MF(c1); }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+    r = sum16(c0) + sum16(c1);
+  } else if (w >= 4 && MODE != 0) {
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < iters; ++it) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint4 v = buf[(lane + 64 * j + it) & 1023];
+        acc.x ^= v.x; acc.y += v.y; acc.z ^= v.z; acc.w += v.w;
+      }
+    }
+    r = (float)(acc.x + acc.y + acc.z + acc.w);
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+#undef MF
+#undef EX
+
+// Placement: each group records its XCD id and hardware id (SE, SH, CU
+// fields) and spins for a fixed number of clocks so that all groups of the
+// launch are resident together, as the first round of a real launch is.
+__global__ __launch_bounds__(kThreads) void k_place(uint2* out, long long spin) {
+  unsigned xcc, hwid;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hwid));
+  const long long t0 = clock64();
+  while (clock64() - t0 < spin) {
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = make_uint2(xcc, hwid);
 }
 
 __global__ __launch_bounds__(kThreads) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
@@ -203,7 +293,30 @@ int main() {
   const float t_exp = time_ms([&] { hipLaunchKernelGGL(k_valu<true>, dim3(grid), dim3(kThreads), 0, 0, out, it_v, 1e-3f); });
   const float t_fma = time_ms([&] { hipLaunchKernelGGL(k_valu<false>, dim3(grid), dim3(kThreads), 0, 0, out, it_v, 1e-3f); });
   const float t_mix = time_ms([&] { hipLaunchKernelGGL(k_overlap<0>, dim3(grid), dim3(kThreads), 0, 0, out, it_o, 1e-3f); });
-  const float t_split = time_ms([&] { hipLaunchKernelGGL(k_overlap<1>, dim3(grid), dim3(kThreads), 0, 0, out, it_o, 1e-3f); });
+  // split: one 8-wave group per CU (waves_per_simd = 2 waves on each SIMD, one of each kind)
+  const float t_split = time_ms([&] { hipLaunchKernelGGL(k_overlap<1>, dim3(cus), dim3(2 * kThreads), 0, 0, out, it_o, 1e-3f); });
+  const int it_f = 4000;
+  const float t_row = time_ms([&] { hipLaunchKernelGGL(k_lds_frag<true>, dim3(grid), dim3(kThreads), 0, 0, out, it_f); });
+  const float t_col = time_ms([&] { hipLaunchKernelGGL(k_lds_frag<false>, dim3(grid), dim3(kThreads), 0, 0, out, it_f); });
+  const double frag_bytes = (double)grid * kThreads * it_f * 128;  // 128 bytes per lane per iteration in both kinds
+  const int it_ml = 8000;
+  const float t_ml_p = time_ms([&] { hipLaunchKernelGGL(k_mfma_lds<0>, dim3(cus), dim3(2 * kThreads), 0, 0, out, it_ml, 1e-3f); });
+  const float t_ml_b = time_ms([&] { hipLaunchKernelGGL(k_mfma_lds<1>, dim3(cus), dim3(2 * kThreads), 0, 0, out, it_ml, 1e-3f); });
+  const float t_ml_l = time_ms([&] { hipLaunchKernelGGL(k_mfma_lds<2>, dim3(cus), dim3(2 * kThreads), 0, 0, out, it_ml, 1e-3f); });
+
+  const int pgrid = 6 * cus;
+  uint2* place = nullptr;
+  CHECK(hipMalloc(&place, (size_t)pgrid * sizeof(uint2)));
+  hipLaunchKernelGGL(k_place, dim3(pgrid), dim3(kThreads), 0, 0, place, 2000000LL);
+  CHECK(hipGetLastError());
+  std::vector<uint2> ph(pgrid);
+  CHECK(hipMemcpy(ph.data(), place, (size_t)pgrid * sizeof(uint2), hipMemcpyDeviceToHost));
+  CHECK(hipFree(place));
+  // HW_ID fields: CU bits 11:8, SH bit 12, SE bits 15:13 (identify a CU within its XCD)
+  auto cu_of = [&](int g) { return std::make_pair(ph[g].x, (ph[g].y >> 8) & 0xff); };
+  int xcd_mod8 = 0, same_cu = 0;
+  for (int g = 0; g < pgrid; ++g) xcd_mod8 += (int)ph[g].x == g % 8;
+  for (int g = 0; g + 256 < pgrid; ++g) same_cu += cu_of(g) == cu_of(g + 256);
   const float t_lds = time_ms([&] { hipLaunchKernelGGL(k_lds, dim3(grid), dim3(kThreads), 0, 0, reinterpret_cast<unsigned*>(out), it_l); });
 
   // Products per wave: it*8; exponentials per wave: it*32 (mix and split alike).
@@ -242,12 +355,18 @@ int main() {
       "\"exp_ns_per_wave_instr\": %.3f, \"fma_ns_per_wave_instr\": %.3f, "
       "\"mix_over_longer\": %.3f, \"split_over_longer\": %.3f, "
       "\"lds_read_tbs\": %.1f, \"lds_bytes_per_cu_ns\": %.1f, "
+      "\"lds_row_frag_bytes_per_cu_ns\": %.1f, \"lds_col_frag_bytes_per_cu_ns\": %.1f, "
+      "\"mfma_with_lds_reader_over_longer\": %.3f, "
+      "\"placement\": {\"groups\": %d, \"xcd_is_group_mod_8\": %.4f, \"group_and_group_plus_256_share_cu\": %.4f}, "
       "\"hbm_copy_tbs\": %.2f, \"atomic_f32_gops\": %.1f, "
       "\"ms\": {\"mfma\": %.4f, \"exp\": %.4f, \"fma\": %.4f, \"mix\": %.4f, \"split\": %.4f, \"lds\": %.4f, "
-      "\"copy\": %.4f, \"atomic\": %.4f}}\n",
+      "\"copy\": %.4f, \"atomic\": %.4f, \"lds_row_frag\": %.4f, \"lds_col_frag\": %.4f, "
+      "\"mfma_alone\": %.4f, \"lds_alone\": %.4f, \"mfma_with_lds\": %.4f}}\n",
       prop.gcnArchName, cus, waves_per_simd, mfma_flops / (t_mfma * 1e9), mfma_ns, exp_ns, fma_ns,
       t_mix / std::max(o_mfma, o_exp), t_split / std::max(o_mfma, o_exp), lds_bytes / (t_lds * 1e9),
-      lds_bytes / (t_lds * 1e6) / cus, 2.0 * copy_bytes / (t_copy * 1e9), atomics / (t_atomic * 1e6), t_mfma, t_exp,
-      t_fma, t_mix, t_split, t_lds, t_copy, t_atomic);
+      lds_bytes / (t_lds * 1e6) / cus, frag_bytes / (t_row * 1e6) / cus, frag_bytes / (t_col * 1e6) / cus,
+      t_ml_b / std::max(t_ml_p, t_ml_l), pgrid, (double)xcd_mod8 / pgrid, (double)same_cu / (pgrid - 256),
+      2.0 * copy_bytes / (t_copy * 1e9), atomics / (t_atomic * 1e6), t_mfma, t_exp,
+      t_fma, t_mix, t_split, t_lds, t_copy, t_atomic, t_row, t_col, t_ml_p, t_ml_l, t_ml_b);
   return 0;
 }

@@ -14,7 +14,10 @@ Prints one JSON line.  Besides the whole-step rate it carries:
                 algorithmic FLOPs (2*N^2*d per matrix product per head, halved
                 when causal, times the products the method needs: 2 forward,
                 5 backward -- S, dP, dV, dK, dQ) over its average duration,
-                timed with HIP events on the stream the kernels run on.  The
+                timed with HIP events on the stream the kernels run on, in
+                the timed region, on every SAMPLE_EVERY-th step only (each
+                event record costs the stream a few microseconds; recording
+                them on every step would inflate the step time).  The
                 gradient kernel executes 7 products (its dQ blocks recompute S
                 and dP); that rate is reported beside it as
                 `executed_tflops`, never as `achieved`.  `traffic` is the HBM
@@ -65,6 +68,11 @@ KERNELS = {
     # backward: S, dP, dV, dK, dQ; the dQ blocks recompute S and dP (4 + 3)
     "bwd_grad_kernel": ("io_aware_exact_07_amd/csrc/fa_bwd.hip", 5, 7),
 }
+
+
+# Steps of the timed region that also record per-stage events (fwd_ms,
+# bwd_stage_ms and the roofline's launch duration): one in SAMPLE_EVERY.
+SAMPLE_EVERY = 10
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -462,19 +470,24 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    starts = [mk() for _ in range(K)]
-    marks = [[mk(), mk(), mk()] for _ in range(K)]
+    # Per-stage events on every SAMPLE_EVERY-th timed step (at least one).
+    sampled = list(range(0, K, SAMPLE_EVERY))
+    starts = {i: mk() for i in sampled}
+    marks = {i: [mk(), mk(), mk()] for i in sampled}
     t_begin, t_end = mk(), mk()
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(K):
-        starts[i].record(stream)
-        step(marks[i])
+        if i in starts:
+            starts[i].record(stream)
+            step(marks[i])
+        else:
+            step()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     ms = total_ms / K
-    avg = lambda f: sum(f(i) for i in range(K)) / K
+    avg = lambda f: sum(f(i) for i in sampled) / len(sampled)
     fwd_ms = avg(lambda i: starts[i].elapsed_time(marks[i][0]))
     prep_ms = avg(lambda i: marks[i][0].elapsed_time(marks[i][1]))
     grads_ms = avg(lambda i: marks[i][1].elapsed_time(marks[i][2]))
@@ -534,6 +547,7 @@ def main():
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
         "bwd_stage_ms": {"prepare": round(prep_ms, 5), "dkdv_dq": round(grads_ms, 5)},
+        "stage_timing": {"steps_with_events": len(sampled), "one_in": SAMPLE_EVERY},
         **({"cold_cache": cold} if cold is not None else {}),
         "effective_tflops": (round(value * float((sl.double() ** 2).sum()) / (B * N * N), 3) if sl is not None
                              else None),
@@ -554,6 +568,7 @@ def main():
             "traffic": traffic,
             "traffic_gbs": None if traffic is None else round(traffic / (launches[dom] * 1e-3) / 1e9, 1),
             "avg_launch_ms": round(launches[dom], 5),
+            "launches_timed": len(sampled),
         },
     }
     if not args.no_cpu_baseline:

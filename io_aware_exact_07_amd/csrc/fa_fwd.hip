@@ -75,7 +75,10 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 ? 2 : 1)) void fwd_ker
   // and each XCD runs its blocks heaviest first (causal work grows with the
   // query block index).  Workgroups g and g + kCUs share a compute unit, so
   // under the causal mask every other group of kCUs is reversed to pair heavy
-  // with light blocks there.
+  // with light blocks there.  At bf16 d = 64 and 96 a compute unit holds three
+  // workgroups (g + 2*kCUs too); the pairing then balances two of the three,
+  // which measured the same as a three-way balance, because a causal launch's
+  // span is set by its heaviest blocks rather than by compute-unit load.
   int bh, qb;
   place_workgroup(make_placement(BH, nqb), blockIdx.x, CAUSAL ? kCUs / 8 : 0, bh, qb);
   const int b = bh / a.H;

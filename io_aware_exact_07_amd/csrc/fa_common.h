@@ -249,40 +249,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Copies rows [r0, r0+R) of a row-major [nrows][D] global array into an LDS
-// tile with row stride STR, through registers so the global load can be
-// issued early and the LDS store later.  Rows >= nrows are zero-filled.
-template <typename T, int R, int D, int NT>
-struct TileCopy {
-  static constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;          // chunks per row
-  static constexpr int TOTAL = R * CPR;
-  static_assert(TOTAL % NT == 0, "tile must split evenly over the threads");
-  static constexpr int PER = TOTAL / NT;
-  uint4 buf[PER];
-
-  __device__ __forceinline__ void load(const T* g, int r0, int nrows, int tid) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + u * NT;
-      const int row = c / CPR, col = (c % CPR) * EPC;
-      if (r0 + row < nrows)
-        buf[u] = *reinterpret_cast<const uint4*>(g + (size_t)(r0 + row) * D + col);
-      else
-        buf[u] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  // Into a swizzled Tile<T, D> layout.
-  __device__ __forceinline__ void store(T* lds, int tid) const {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + u * NT;
-      const int row = c / CPR, col = (c % CPR) * EPC;
-      *reinterpret_cast<uint4*>(lds + Tile<T, D>::off(row, col)) = buf[u];
-    }
-  }
-};
-
 // One global_load_lds_dwordx4: every active lane copies 16 bytes from its
 // `src` to dst + 16 * lane, where dst (wave-uniform) goes in M0.  Issued
 // through asm so that the compiler's LDS-DMA tracking, which cannot tell the

@@ -220,6 +220,12 @@ __device__ __forceinline__ void dkdv_block(const BwdArgs& a, const int kb, const
     auto tiles = [&](auto EDGE) {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
+      // A query tile whose queries all precede this wave's keys (in the
+      // diagonal block, the first w tiles of wave w) has P = 0 and dS = 0
+      // everywhere: its products would add exact zeros, so they are skipped.
+      if constexpr (CAUSAL && decltype(EDGE)::value) {
+        if (q0 + 32 * qt + 31 < kw0) continue;
+      }
       // dP starts from -D of each query row, so the product leaves dP - D.
       f32x16 s = zero16(), dp;
 #pragma unroll
@@ -308,14 +314,15 @@ struct DqShape {
 };
 
 // One query block (BQ queries of head bh): dQ.  `lds` holds S stages of
-// [K tile | V tile].  G = 32-key tiles whose scores are live at once: the
+// [K tile | V tile].  GMAX = 32-key tiles whose scores are live at once: the
 // whole block, or one tile at a time where the register budget is halved.
-template <typename T, int D, bool CAUSAL, int G>
+template <typename T, int D, bool CAUSAL, int GMAX>
 __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const int bh, char* lds) {
   using SH = DqShape<T, D>;
   constexpr int BQ = SH::BQ, BK = SH::BK, NT = kThreads;
   constexpr int NC = D / 16;
   constexpr int NDT = D / 32;
+  constexpr int NKT = BK / 32;  // 32-key tiles per block
   // Pipeline stages as in the forward kernel: K/V blocks copied HBM -> LDS
   // S-1 blocks ahead.
   constexpr int S = SH::S;
@@ -394,11 +401,15 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
     // Two versions of the block body keep the masking branch out of it, so
     // the scheduler can overlap one tile's exponentials with the other
     // tile's matrix products.
-    auto body = [&](auto EDGE) {
-    constexpr int NKT = BK / 32;  // 32-key tiles per block
+    // `ntile` of the block's 32-key tiles take part; the rest are wholly
+    // masked for this wave (past the sequence end or above its queries), so
+    // their products would add exact zeros and are skipped.
+    auto body = [&](auto EDGE, auto GGc, const int ntile) {
+    constexpr int G = decltype(GGc)::value;  // tiles whose scores are live at once
     static_assert(NKT % G == 0, "tile groups must divide the block");
 #pragma unroll
     for (int g0 = 0; g0 < NKT; g0 += G) {
+      if (g0 >= ntile) break;
       f32x16 s[G], dp[G];
 #pragma unroll
       for (int t = 0; t < G; ++t) {
@@ -437,8 +448,18 @@ __device__ __forceinline__ void dq_block(const BwdArgs& a, const int qb, const i
         for (int c = 0; c < 2 * G; ++c) mma16(acc[t], fr.col(kt, 32 * g0 + 16 * c, t), dsf[c]);
     }
     };
-    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) body(std::true_type());
-    else body(std::false_type());
+    if ((k0 + BK > L) || (CAUSAL && k0 + BK - 1 > q0w)) {
+      // Tiles wholly above this wave's queries are skipped under the causal
+      // mask; tiles wholly past the sequence end only where two tiles are
+      // grouped (one at a time, the extra branch costs registers at d > 64).
+      int live = NKT;
+      if (CAUSAL || GMAX > 1) live = min(live, (L - k0 + 31) / 32);
+      if (CAUSAL) live = min(live, (q0w + 63 - k0) / 32);
+      if (GMAX > 1 && live < NKT) body(std::true_type(), std::integral_constant<int, 1>(), live);
+      else body(std::true_type(), std::integral_constant<int, GMAX>(), live);
+    } else {
+      body(std::false_type(), std::integral_constant<int, GMAX>(), NKT);
+    }
   };
   for (int kb = 0; kb < nkb; kb += S)
     static_for<S>([&](auto J) {

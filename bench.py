@@ -27,6 +27,7 @@ Prints one JSON line.  Besides the whole-step rate it carries:
   cpu_baseline  the fp64 CPU oracle timed on this host on whole heads of the
                 same workload (about 10 s of work), in the same unit
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       (without --warmup: untimed steps for at least 1 s and 10 steps before timing)
                        [--workload gpt2_long|gpt2_small|bert_large|very_long|single_head]
                        [--head-dim 64|96|128] [--cold]
        (the same JSON line for another workload; `traffic` is reported only
@@ -73,6 +74,28 @@ KERNELS = {
 # Steps of the timed region that also record per-stage events (fwd_ms,
 # bwd_stage_ms and the roofline's launch duration): one in SAMPLE_EVERY.
 SAMPLE_EVERY = 10
+# Default warm-up: at least 10 steps and this much wall time, GPU-synchronised.
+WARM_SECONDS = 1.0
+
+
+def warm_up(step, warmup, sync) -> int:
+    """Untimed steps before the timed region: exactly `warmup` if given, else
+    at least 10 steps and WARM_SECONDS of GPU time, so that the GPU clocks reach
+    the steady state a training loop runs at (after only 10 steps the
+    GPT-2-small step read 17 % slower, the long-context step 4 %).  Returns the
+    number of steps run."""
+    if warmup is not None:
+        for _ in range(warmup):
+            step()
+        sync()
+        return warmup
+    n, t0 = 0, time.time()
+    while n < 10 or time.time() - t0 < WARM_SECONDS:
+        for _ in range(10):
+            step()
+        n += 10
+        sync()
+    return n
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -266,7 +289,7 @@ def hbm_model_bytes(B, H, N, d, e, causal):
             "grad_compulsory": int(grad_c), "grad_tiled_model": int(grad_t)}
 
 
-def sweep(steps=20, warmup=5):
+def sweep(steps=20, warmup=None):
     """fwd+bwd rate over sequence lengths at a fixed token count: H=12, d=64,
     causal, N = 1k .. 32k, B = 16384 / N (B = 1 at N = 32k; one JSON line per N,
     with the compulsory and tiled-model HBM bytes per launch of both kernels)."""
@@ -284,9 +307,7 @@ def sweep(steps=20, warmup=5):
             o, lse = fa.forward(q, k, v, causal=True)
             fa.backward(q, k, v, o, do, lse, causal=True)
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
+        n_warm = warm_up(step, warmup, torch.cuda.synchronize)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
@@ -298,7 +319,7 @@ def sweep(steps=20, warmup=5):
         print(json.dumps({"mode": "sweep", "workload": w.name, "B": B, "N": N, "ms_per_step": round(ms, 5),
                           "tflops": round((f_fwd + f_bwd) / (ms * 1e-3) / 1e12, 3),
                           "pct_peak": round(100 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                          "launches_per_kernel": warmup + steps,
+                          "launches_per_kernel": n_warm + steps,
                           "hbm_model_bytes": hbm_model_bytes(B, 12, N, 64, 2, True)}),
               flush=True)
         del q, k, v, do
@@ -385,7 +406,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 10 steps and 1 s, so the GPU clocks settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--memory-scaling", action="store_true",
@@ -419,7 +441,7 @@ def main():
         compare_explicit()
         return
     if args.sweep:
-        sweep(steps=min(args.steps, 20), warmup=min(args.warmup, 5))
+        sweep(steps=min(args.steps, 20), warmup=None if args.warmup is None else min(args.warmup, 5))
         return
     if args.calibrate:
         calibrate()
@@ -465,9 +487,7 @@ def main():
         if st != 0:
             raise RuntimeError(f"attention call failed: {st}")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm_up(step, args.warmup, torch.cuda.synchronize)
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
     # Per-stage events on every SAMPLE_EVERY-th timed step (at least one).
@@ -535,7 +555,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

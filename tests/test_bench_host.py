@@ -63,3 +63,26 @@ def test_hbm_model_reproduces_the_committed_traffic_records():
     # block pairs beyond the first read, per head (nb^2/2 - nb with nb = N/128),
     # times heads: 112 * 96 at N = 2048, 480 * 48 at N = 4096
     assert reread_a * 480 * 48 == reread_b * 112 * 96
+
+
+def test_warm_up_runs_exactly_w_steps_when_given_else_until_time_and_ten_steps(monkeypatch):
+    calls = {"step": 0, "sync": 0}
+
+    def step():
+        calls["step"] += 1
+
+    def sync():
+        calls["sync"] += 1
+
+    assert bench.warm_up(step, 3, sync) == 3 and calls["step"] == 3
+    assert bench.warm_up(step, 0, sync) == 0 and calls["step"] == 3
+    # Default: whole groups of ten, synchronised, until both 10 steps and WARM_SECONDS have passed.
+    monkeypatch.setattr(bench, "WARM_SECONDS", 0.0)
+    calls["step"] = 0
+    assert bench.warm_up(step, None, sync) == 10 and calls["step"] == 10
+    clock = iter([0.0, 0.1, 0.2, 0.35, 0.6])
+    monkeypatch.setattr(bench, "WARM_SECONDS", 0.3)
+    monkeypatch.setattr(bench.time, "time", lambda: next(clock))
+    calls["step"] = 0
+    n = bench.warm_up(step, None, sync)
+    assert n == calls["step"] == 30  # t = 0.1, 0.2 after the first two groups, 0.35 >= 0.3 after the third

@@ -230,3 +230,40 @@ def test_explicit_baseline_matches_the_oracle(causal, seqlens):
                 g = f64(t[b, h])
                 assert rel_err(g[:L], ref[name][b, h][:L]) <= tol[name], (name, b, h)
                 assert np.all(g[L:] == 0), (name, b, h)
+
+
+def test_bench_line_carries_consistent_contract_fields():
+    """One short `bench.py` run on its default workload prints one JSON line
+    whose rate, stage times and roofline agree with each other: value is the
+    counted FLOPs over ms_per_step, achieved is the gradient launch's
+    algorithmic FLOPs over its average duration, frac is achieved over the
+    bf16 peak, and that duration fits inside a step."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("bench.py --steps 5 --warmup 2 --no-cpu-baseline", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "5", "--warmup", "2",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout
+    rec = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 5 and rec["warmup"] == 2
+    assert rec["unit"] == "TFLOP/s" and rec["higher_is_better"] is True and rec["dtype"] == "bf16"
+    cfg = rec["config"]
+    assert (cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"]) == (1, 12, 8192, 64, True)
+    counted = cfg["fwd_gflop"] + cfg["bwd_gflop"]                      # GFLOP per step
+    assert math.isclose(rec["value"], counted / rec["ms_per_step"], rel_tol=2e-3)
+    rf = rec["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
+    assert rf["kernel"] == "bwd_grad_kernel"
+    assert math.isclose(rf["algorithmic_gflop_per_launch"], cfg["bwd_gflop"], rel_tol=1e-6)
+    assert math.isclose(rf["achieved"], rf["algorithmic_gflop_per_launch"] / rf["avg_launch_ms"], rel_tol=2e-3)
+    assert math.isclose(rf["frac"], rf["achieved"] / rf["peak"], rel_tol=2e-3)
+    assert 0 < rf["avg_launch_ms"] < rec["ms_per_step"] * 1.5
+    assert rf["traffic"] is None or rf["traffic"] > 0

@@ -255,8 +255,7 @@ def compare_explicit(steps=10):
 
         res = {"mode": "compare_explicit", "workload": w.name}
         for name, fn in (("tiled", ours), ("explicit", explicit)):
-            fn()
-            torch.cuda.synchronize()
+            warm_up(fn, None, torch.cuda.synchronize)  # both sides timed with settled clocks
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             for _ in range(steps):

@@ -24,7 +24,9 @@
  * d fastest, of element type `dtype`, on the device, 16-byte aligned.
  * lse is a contiguous float32 [B, H, N] device array.  seqlens is NULL (every
  * sequence has length N) or a device int32 [B] array; each value is clamped
- * to [0, N] on the device.
+ * to [0, N] on the device.  Sizes: N <= 2^24, B*H <= 2^31 - 1 and
+ * 2*B*H*ceil(N/128) <= 2^31 - 1 (the largest launch grid); larger sizes return
+ * FA_ERR_INVALID_ARG.
  *
  * Ownership: the caller allocates and frees every buffer, including the
  * backward workspace; the library never allocates or frees device memory and
@@ -59,7 +61,7 @@ typedef enum {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scale or dtype */
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative or too large size, bad scale or dtype */
   FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64, 96 or 128 */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_bytes() */
   FA_ERR_HIP = -4,         /* a kernel launch failed */

@@ -23,6 +23,9 @@ int check_common(int B, int H, int N, int d, float scale, int dtype) {
   if (!(isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  // The largest launch (the interleaved gradient lists) has 2 workgroups per
+  // head and 128-row block; its grid must fit a 32-bit dimension.
+  if (2LL * B * H * ((N + 127) / 128) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   if (B == 0 || H == 0 || N == 0) return 1;
   return FA_OK;
 }

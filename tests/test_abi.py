@@ -59,6 +59,8 @@ def bwd(**kw):
     (dict(B=-1), fa.FA_ERR_INVALID_ARG),
     (dict(N=-5), fa.FA_ERR_INVALID_ARG),
     (dict(N=(1 << 24) + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 16, H=1 << 16), fa.FA_ERR_INVALID_ARG),   # B*H beyond 2^31 - 1
+    (dict(H=1 << 15, N=1 << 24), fa.FA_ERR_INVALID_ARG),   # 2*B*H*ceil(N/128) = 2^33 workgroups
     (dict(B=0), fa.FA_OK),                              # empty: nothing to do, nothing launched
     (dict(N=0, q=None), fa.FA_OK),
 ])
@@ -73,6 +75,7 @@ def test_forward_validation(kw, status):
     (dict(workspace_bytes=100), fa.FA_ERR_WORKSPACE),
     (dict(workspace=FAKE + 8), fa.FA_ERR_WORKSPACE),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=1 << 15, N=1 << 24), fa.FA_ERR_INVALID_ARG),   # launch grid beyond 32 bits
     (dict(H=0), fa.FA_OK),
 ])
 def test_backward_validation(kw, status):

@@ -139,11 +139,13 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
  *            dk and dv (reads q, k, v, dO, lse and the prepared workspace).
  *   dq:      recomputes the score blocks query block by query block and
  *            writes dq (same inputs).
- *   dkdv_dq: both of the above.  With a causal mask or seqlens, and up to
- *            128 MiB of streamed operands (4*B*H*N*d elements), it is one
- *            launch that interleaves the two block lists heaviest first (a
- *            lone list's heaviest blocks outlast the average load of a
- *            resident workgroup); otherwise it is dkdv then dq on `stream`.
+ *   dkdv_dq: both of the above.  With a causal mask or seqlens, and with
+ *            streamed operands (4*B*H*N*d elements) of at most 64 MiB, or at
+ *            most 128 MiB when N <= 2048, it is one launch that interleaves
+ *            the two block lists heaviest first (a lone list's heaviest
+ *            blocks outlast the average load of a resident workgroup);
+ *            otherwise it is dkdv then dq on `stream`.  Either way the
+ *            gradients are bitwise the same.
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */

@@ -110,15 +110,19 @@ int run_stage(int stage, const fa::BwdArgs& a, int d, int dtype, int causal, voi
 // Both gradient stages.  Under a causal mask or per-sequence lengths the
 // blocks of a lone dK/dV or dQ launch differ in work, and its heaviest blocks
 // run on after the rest of the grid has drained; one launch that interleaves
-// the two lists heaviest first evens the load out.  With equal blocks there
-// is nothing to even out, and when the operands the two lists stream (Q, dO
-// and K, V of every head) no longer fit the 256 MB last-level cache
-// together, running the lists one after the other keeps each list's working
-// set resident; both cases take two launches.
+// the two lists heaviest first evens the load out.  That pays for short
+// sequences and small problems.  Otherwise the two lists run one after the
+// other: with equal blocks there is nothing to even out, the single-list
+// launches place each head's blocks on as few XCDs as possible (fewer L2
+// misses), and once the operands the two lists stream (Q, dO and K, V of
+// every head) outgrow the last-level cache together, each list's working set
+// stays resident.  Measured: one launch is ahead at N <= 2048 and at 64 MiB
+// or less, level from there to 128 MiB at N >= 4096, and behind beyond.
 int run_grads(const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
   const double streamed = 4.0 * a.B * a.H * (double)a.N * d * (dtype == FA_BF16 ? 2 : 4);
   const bool uneven = causal || a.seqlens != nullptr;
-  if (uneven && streamed <= 128.0 * (1 << 20)) return run_stage(kGrads, a, d, dtype, causal, stream);
+  const bool small = streamed <= 64.0 * (1 << 20) || (a.N <= 2048 && streamed <= 128.0 * (1 << 20));
+  if (uneven && small) return run_stage(kGrads, a, d, dtype, causal, stream);
   const int st = run_stage(kDkDv, a, d, dtype, causal, stream);
   if (st != FA_OK) return st;
   return run_stage(kDq, a, d, dtype, causal, stream);

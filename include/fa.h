@@ -141,11 +141,11 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
  *            writes dq (same inputs).
  *   dkdv_dq: both of the above.  With a causal mask or seqlens, and with
  *            streamed operands (4*B*H*N*d elements) of at most 64 MiB, or at
- *            most 128 MiB when N <= 2048, it is one launch that interleaves
- *            the two block lists heaviest first (a lone list's heaviest
- *            blocks outlast the average load of a resident workgroup);
- *            otherwise it is dkdv then dq on `stream`.  Either way the
- *            gradients are bitwise the same.
+ *            most 128 MiB when N <= 2048 or at bf16 d = 128, it is one
+ *            launch that interleaves the two block lists heaviest first (a
+ *            lone list's heaviest blocks outlast the average load of a
+ *            resident workgroup); otherwise it is dkdv then dq on `stream`.
+ *            Either way the gradients are bitwise the same.
  * Validation and errors are as for fa_bwd; each stage checks only the
  * pointers it uses (the others may be NULL).
  */

@@ -117,11 +117,14 @@ int run_stage(int stage, const fa::BwdArgs& a, int d, int dtype, int causal, voi
 // misses), and once the operands the two lists stream (Q, dO and K, V of
 // every head) outgrow the last-level cache together, each list's working set
 // stays resident.  Measured: one launch is ahead at N <= 2048 and at 64 MiB
-// or less, level from there to 128 MiB at N >= 4096, and behind beyond.
+// or less, level from there to 128 MiB at N >= 4096, and behind beyond.  At
+// bf16 d = 128 the dK/dV-only launch runs one wave per SIMD while the
+// interleaved one runs two, so there one launch stays ahead up to 128 MiB.
 int run_grads(const fa::BwdArgs& a, int d, int dtype, int causal, void* stream) {
   const double streamed = 4.0 * a.B * a.H * (double)a.N * d * (dtype == FA_BF16 ? 2 : 4);
   const bool uneven = causal || a.seqlens != nullptr;
-  const bool small = streamed <= 64.0 * (1 << 20) || (a.N <= 2048 && streamed <= 128.0 * (1 << 20));
+  const bool small = streamed <= 64.0 * (1 << 20) ||
+                     ((a.N <= 2048 || (dtype == FA_BF16 && d == 128)) && streamed <= 128.0 * (1 << 20));
   if (uneven && small) return run_stage(kGrads, a, d, dtype, causal, stream);
   const int st = run_stage(kDkDv, a, d, dtype, causal, stream);
   if (st != FA_OK) return st;
